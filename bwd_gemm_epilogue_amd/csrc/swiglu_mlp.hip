@@ -1,0 +1,573 @@
+// swiglu_mlp.hip -- the SwiGLU MLP training step on gfx950, behind the C ABI
+// declared in include/swiglu_mlp.h.
+//
+// Forward (the drop-h report, forward skeleton): GEMM-1 with a SwiGLU
+// epilogue writes preact and a transient h; the down GEMM writes y.
+// Backward (the note "SwiGLU MLP forward principle, backward chain and
+// optimisation", sections 2-4): the dout GEMM runs with the SwiGLU-backward
+// epilogue so dout never reaches HBM, then dW_down, dx and dW1.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "gemm_core.hpp"
+#include "swiglu_math.hpp"
+#include "swiglu_mlp.h"
+
+namespace swg {
+
+// ---------------------------------------------------------------------------
+// Forward GEMM-1 epilogue.  The tile's B columns are paired (left block then
+// the matching gate block), so slab columns [0, BN/2) hold left and
+// [BN/2, BN) the gate of the same intermediate channels.  Stores the bf16
+// preact halves and h = rn(left * silu(gate)) from the rounded values.
+// ---------------------------------------------------------------------------
+struct EpiSwigluFwd {
+  struct Params {
+    uint16_t* preact;  // [M, 2I]
+    uint16_t* h;       // [M, I]
+    int64_t I;
+  };
+  template <class T>
+  struct Prefetch {};
+  template <class T>
+  __device__ static void prefetch(const Params&, const SlabCtx<T>&, Prefetch<T>&, int) {}
+  template <class T>
+  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>&, int tid) {
+    constexpr int HALF = T::BN / 2;
+    constexpr int CPR = HALF / 8;
+    constexpr int ITEMS = T::SLAB_ROWS * CPR;
+    static_assert(ITEMS % T::THREADS == 0, "slab items must split evenly");
+#pragma unroll
+    for (int k = 0; k < ITEMS / T::THREADS; ++k) {
+      const int it = tid + k * T::THREADS;
+      const int sr = it / CPR, ch = it % CPR;
+      const int row = c.row(sr);
+      const int64_t i0 = (int64_t)c.tn * HALF + ch * 8;
+      if (row < c.M) {
+        const u32x4 lp = pack8(c.read8(sr, ch * 8));
+        const u32x4 gp = pack8(c.read8(sr, HALF + ch * 8));
+        const f32x8 left = unpack8(lp), gate = unpack8(gp);
+        f32x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = swiglu_h(left[e], gate[e]);
+        uint16_t* pr = p.preact + (int64_t)row * 2 * p.I;
+        *(u32x4*)(pr + i0) = lp;
+        *(u32x4*)(pr + p.I + i0) = gp;
+        *(u32x4*)(p.h + (int64_t)row * p.I + i0) = pack8(h);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Fused dgrad epilogue (the centre of the method).  The slab holds fp32 dout
+// for intermediate channels [tn*BN, tn*BN + BN).  For each 8-channel chunk it
+// reads left = preact[:, i] and gate = preact[:, I + i] (issued before the
+// slab is staged so the loads overlap the LDS traffic), recomputes sigma,
+// silu and silu', and writes
+//   grad_preact[:, i]     = dout * silu(gate)
+//   grad_preact[:, I + i] = dout * left * silu'(gate)
+//   h[:, i]               = rn(left * silu(gate))
+// ---------------------------------------------------------------------------
+struct EpiSwigluBwd {
+  struct Params {
+    const uint16_t* preact;  // [M, 2I]
+    uint16_t* grad_preact;   // [M, 2I]
+    uint16_t* h;             // [M, I]
+    int64_t I;
+  };
+  template <class T>
+  struct Prefetch {
+    static constexpr int N = T::SLAB_ROWS * (T::BN / 8) / T::THREADS;
+    u32x4 left[N], gate[N];
+  };
+  template <class T>
+  __device__ static void prefetch(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
+    constexpr int CPR = T::BN / 8;
+#pragma unroll
+    for (int k = 0; k < Prefetch<T>::N; ++k) {
+      const int it = tid + k * T::THREADS;
+      const int sr = it / CPR, ch = it % CPR;
+      const int row = c.row(sr);
+      const int64_t i0 = (int64_t)c.tn * T::BN + ch * 8;
+      if (row < c.M) {
+        const uint16_t* pr = p.preact + (int64_t)row * 2 * p.I;
+        pf.left[k] = __builtin_nontemporal_load((const u32x4*)(pr + i0));
+        pf.gate[k] = __builtin_nontemporal_load((const u32x4*)(pr + p.I + i0));
+      }
+    }
+  }
+  template <class T>
+  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
+    constexpr int CPR = T::BN / 8;
+#pragma unroll
+    for (int k = 0; k < Prefetch<T>::N; ++k) {
+      const int it = tid + k * T::THREADS;
+      const int sr = it / CPR, ch = it % CPR;
+      const int row = c.row(sr);
+      const int64_t i0 = (int64_t)c.tn * T::BN + ch * 8;
+      if (row < c.M) {
+        const f32x8 dout = c.read8(sr, ch * 8);
+        const f32x8 left = unpack8(pf.left[k]), gate = unpack8(pf.gate[k]);
+        f32x8 dl, dg, h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const Act a = sw_act(gate[e]);
+          dl[e] = dout[e] * a.silu;
+          dg[e] = (dout[e] * left[e]) * a.dsilu;
+          h[e] = left[e] * a.silu;
+        }
+        uint16_t* gpr = p.grad_preact + (int64_t)row * 2 * p.I;
+        *(u32x4*)(gpr + i0) = pack8(dl);
+        *(u32x4*)(gpr + p.I + i0) = pack8(dg);
+        *(u32x4*)(p.h + (int64_t)row * p.I + i0) = pack8(h);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Baseline elementwise SwiGLU backward (the drop-h report's fused
+// h / grad_preact kernel as its own pass): one 8-channel chunk per thread.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) swiglu_bwd_elementwise_kernel(const uint16_t* __restrict__ preact,
+                                                                     const uint16_t* __restrict__ dout,
+                                                                     uint16_t* __restrict__ grad_preact,
+                                                                     uint16_t* __restrict__ h, int64_t M,
+                                                                     int64_t I) {
+  const int64_t chunks_per_row = I / 8;
+  const int64_t total = M * chunks_per_row;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = t / chunks_per_row, i0 = (t % chunks_per_row) * 8;
+    const uint16_t* pr = preact + row * 2 * I;
+    const f32x8 left = unpack8(*(const u32x4*)(pr + i0));
+    const f32x8 gate = unpack8(*(const u32x4*)(pr + I + i0));
+    const f32x8 d = unpack8(*(const u32x4*)(dout + row * I + i0));
+    f32x8 dl, dg, hh;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const Act a = sw_act(gate[e]);
+      dl[e] = d[e] * a.silu;
+      dg[e] = (d[e] * left[e]) * a.dsilu;
+      hh[e] = left[e] * a.silu;
+    }
+    uint16_t* gpr = grad_preact + row * 2 * I;
+    *(u32x4*)(gpr + i0) = pack8(dl);
+    *(u32x4*)(gpr + I + i0) = pack8(dg);
+    *(u32x4*)(h + row * I + i0) = pack8(hh);
+  }
+}
+
+__global__ void __launch_bounds__(256) swiglu_act_eval_kernel(const uint16_t* __restrict__ g,
+                                                              float* __restrict__ sigma,
+                                                              float* __restrict__ silu,
+                                                              float* __restrict__ dsilu, int64_t n) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+    const float x = __builtin_bit_cast(float, (uint32_t)g[t] << 16);
+    const Act a = sw_act(x);
+    sigma[t] = a.sigma;
+    silu[t] = a.silu;
+    dsilu[t] = a.dsilu;
+  }
+}
+
+// Zero fill (dW outputs of an empty batch).
+__global__ void __launch_bounds__(256) zero_kernel(u32x4* __restrict__ p, int64_t n16) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n16; t += (int64_t)gridDim.x * blockDim.x)
+    p[t] = u32x4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace swg
+
+// ===========================================================================
+// Host side
+// ===========================================================================
+namespace {
+
+using namespace swg;
+
+typedef TileCfg<256, 256, 2, 2> TBig;  // 4 waves, 128x128 per wave
+typedef TileCfg<128, 128, 2, 2> TMid;  // 4 waves, 64x64 per wave
+typedef TileCfg<64, 64, 2, 2> TSmall;  // 4 waves, 32x32 per wave (N % 128 != 0)
+
+// D, I, Dout limit: keeps every in-tile byte offset of a 256-row tile below 2^31
+constexpr int64_t kMaxDim = (int64_t)1 << 20;
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range rng(const void* p, int64_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// every output range must be disjoint from every input and from the other outputs
+int check_alias(const Range* ins, int n_in, const Range* outs, int n_out) {
+  for (int o = 0; o < n_out; ++o) {
+    for (int i = 0; i < n_in; ++i)
+      if (overlap(outs[o], ins[i])) return SWIGLU_ERR_ALIAS;
+    for (int j = o + 1; j < n_out; ++j)
+      if (overlap(outs[o], outs[j])) return SWIGLU_ERR_ALIAS;
+  }
+  return SWIGLU_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// a pointer may be NULL only when its tensor holds no bytes
+bool missing(const void* p, int64_t bytes) { return p == nullptr && bytes > 0; }
+
+int check_inner(int64_t d) {
+  if (d <= 0) return SWIGLU_ERR_SHAPE;
+  if (d % 64 != 0 || d > kMaxDim) return SWIGLU_ERR_UNSUPPORTED;
+  return SWIGLU_OK;
+}
+
+int check_tokens(int64_t M) {
+  if (M < 0) return SWIGLU_ERR_SHAPE;
+  if (M > ((int64_t)1 << 31) - 1) return SWIGLU_ERR_UNSUPPORTED;
+  return SWIGLU_OK;
+}
+
+int check_dims(int64_t M, int64_t D, int64_t I, int64_t Dout) {
+  int s;
+  if ((s = check_tokens(M))) return s;
+  if ((s = check_inner(D))) return s;
+  if ((s = check_inner(I))) return s;
+  if ((s = check_inner(Dout))) return s;
+  return SWIGLU_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int launch_status() { return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_HIP; }
+
+template <class T, bool A_K, bool B_K, class Epi>
+int run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+             int pair_off, const typename Epi::Params& ep, hipStream_t st) {
+  GemmArgs g;
+  g.A = A;
+  g.B = B;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.tiles_m = (int)((M + T::BM - 1) / T::BM);
+  g.tiles_n = pair_off > 0 ? (int)(N / T::BN) : (int)((N + T::BN - 1) / T::BN);
+  g.pair_off = pair_off;
+  const int64_t tiles = (int64_t)g.tiles_m * g.tiles_n;
+  if (tiles == 0) return SWIGLU_OK;
+  hipLaunchKernelGGL((gemm_kernel<T, A_K, B_K, Epi>), dim3((unsigned)tiles), dim3(T::THREADS), 0, st, g, ep);
+  return launch_status();
+}
+
+// Pick the largest tile whose N extent divides the GEMM's N (for the paired
+// forward GEMM-1, whose half tile must divide I).
+template <bool A_K, bool B_K, class Epi>
+int run_gemm_auto(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                  int pair_off, const typename Epi::Params& ep, hipStream_t st) {
+  const int64_t n_unit = pair_off > 0 ? N / 2 : N;  // channels per half for paired tiles
+  const int64_t div = pair_off > 0 ? 2 : 1;
+  if (n_unit % (TBig::BN / div) == 0 && M > 256)
+    return run_gemm<TBig, A_K, B_K, Epi>(A, lda, B, ldb, M, N, K, pair_off, ep, st);
+  if (n_unit % (TMid::BN / div) == 0)
+    return run_gemm<TMid, A_K, B_K, Epi>(A, lda, B, ldb, M, N, K, pair_off, ep, st);
+  return run_gemm<TSmall, A_K, B_K, Epi>(A, lda, B, ldb, M, N, K, pair_off, ep, st);
+}
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+const uint16_t* cu16(const void* p) { return (const uint16_t*)p; }
+uint16_t* u16(void* p) { return (uint16_t*)p; }
+
+// --- steps (no argument checks: callers have validated) --------------------
+
+int step_gemm1(const void* x, const void* W1, void* preact, void* h, int64_t M, int64_t D, int64_t I,
+               hipStream_t st) {
+  EpiSwigluFwd::Params ep{u16(preact), u16(h), I};
+  return run_gemm_auto<true, false, EpiSwigluFwd>(cu16(x), D, cu16(W1), 2 * I, M, 2 * I, D, (int)I, ep, st);
+}
+
+int step_down(const void* h, const void* Wd, void* y, int64_t M, int64_t I, int64_t Dout, hipStream_t st) {
+  EpiStore::Params ep{u16(y), Dout};
+  return run_gemm_auto<true, false, EpiStore>(cu16(h), I, cu16(Wd), Dout, M, Dout, I, 0, ep, st);
+}
+
+int step_dgrad_fused(const void* dy, const void* Wd, const void* preact, void* gp, void* h, int64_t M, int64_t I,
+                     int64_t Dout, hipStream_t st) {
+  EpiSwigluBwd::Params ep{cu16(preact), u16(gp), u16(h), I};
+  return run_gemm_auto<true, true, EpiSwigluBwd>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, 0, ep, st);
+}
+
+int step_dgrad_plain(const void* dy, const void* Wd, void* dout, int64_t M, int64_t I, int64_t Dout,
+                     hipStream_t st) {
+  EpiStore::Params ep{u16(dout), I};
+  return run_gemm_auto<true, true, EpiStore>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, 0, ep, st);
+}
+
+int step_elementwise(const void* preact, const void* dout, void* gp, void* h, int64_t M, int64_t I, hipStream_t st) {
+  const int64_t total = M * (I / 8);
+  if (total == 0) return SWIGLU_OK;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  hipLaunchKernelGGL(swiglu_bwd_elementwise_kernel, dim3((unsigned)blocks), dim3(256), 0, st, cu16(preact),
+                     cu16(dout), u16(gp), u16(h), M, I);
+  return launch_status();
+}
+
+int step_zero(void* p, int64_t bytes, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return SWIGLU_OK;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (u32x4*)p, n16);
+  return launch_status();
+}
+
+int step_dw_down(const void* h, const void* dy, void* dWd, int64_t M, int64_t I, int64_t Dout, hipStream_t st) {
+  if (M == 0) return step_zero(dWd, I * Dout * 2, st);
+  EpiStore::Params ep{u16(dWd), Dout};
+  return run_gemm_auto<false, false, EpiStore>(cu16(h), I, cu16(dy), Dout, I, Dout, M, 0, ep, st);
+}
+
+int step_dx(const void* gp, const void* W1, void* dx, int64_t M, int64_t D, int64_t I, hipStream_t st) {
+  EpiStore::Params ep{u16(dx), D};
+  return run_gemm_auto<true, true, EpiStore>(cu16(gp), 2 * I, cu16(W1), 2 * I, M, D, 2 * I, 0, ep, st);
+}
+
+int step_dw1(const void* x, const void* gp, void* dW1, int64_t M, int64_t D, int64_t I, hipStream_t st) {
+  if (M == 0) return step_zero(dW1, D * 2 * I * 2, st);
+  EpiStore::Params ep{u16(dW1), 2 * I};
+  return run_gemm_auto<false, false, EpiStore>(cu16(x), D, cu16(gp), 2 * I, D, 2 * I, M, 0, ep, st);
+}
+
+#define SW_TRY(expr)                  \
+  do {                                \
+    int _s = (expr);                  \
+    if (_s != SWIGLU_OK) return _s;   \
+  } while (0)
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* swiglu_status_string(int status) {
+  switch (status) {
+    case SWIGLU_OK: return "SWIGLU_OK";
+    case SWIGLU_ERR_NULL: return "SWIGLU_ERR_NULL: a required pointer is NULL";
+    case SWIGLU_ERR_SHAPE: return "SWIGLU_ERR_SHAPE: a dimension is negative or zero";
+    case SWIGLU_ERR_UNSUPPORTED: return "SWIGLU_ERR_UNSUPPORTED: D, I and Dout must be multiples of 64 (and sizes in range)";
+    case SWIGLU_ERR_WORKSPACE: return "SWIGLU_ERR_WORKSPACE: workspace missing or too small";
+    case SWIGLU_ERR_ALIAS: return "SWIGLU_ERR_ALIAS: an output overlaps an input or another output";
+    case SWIGLU_ERR_HIP: return "SWIGLU_ERR_HIP: the HIP runtime reported an error";
+    case SWIGLU_ERR_ALIGN: return "SWIGLU_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    default: return "unknown swiglu status";
+  }
+}
+
+int swiglu_abi_version(void) { return (1 << 16) | 0; }
+
+size_t swiglu_mlp_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
+  if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
+  return align256((size_t)(M * I * 2));
+}
+
+size_t swiglu_mlp_bwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
+  if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
+  return align256((size_t)(M * 2 * I * 2)) + align256((size_t)(M * I * 2));
+}
+
+size_t swiglu_mlp_bwd_unfused_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
+  if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
+  return swiglu_mlp_bwd_workspace(M, D, I, Dout) + align256((size_t)(M * I * 2));
+}
+
+int swiglu_mlp_fwd(const void* x, const void* W1, const void* W_down, void* preact, void* y, void* ws,
+                   size_t ws_bytes, int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(check_dims(M, D, I, Dout));
+  if (missing(x, M * D) || !W1 || !W_down || missing(preact, M * I) || missing(y, M * Dout))
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned16(preact) || !aligned16(y) ||
+      (ws && !aligned16(ws)))
+    return SWIGLU_ERR_ALIGN;
+  const size_t need = swiglu_mlp_fwd_workspace(M, D, I, Dout);
+  if (need > 0 && (!ws || ws_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2)};
+  const Range outs[] = {rng(preact, M * 2 * I * 2), rng(y, M * Dout * 2), rng(ws, (int64_t)need)};
+  SW_TRY(check_alias(ins, 3, outs, 3));
+  hipStream_t st = as_stream(stream);
+  SW_TRY(step_gemm1(x, W1, preact, ws, M, D, I, st));
+  return step_down(ws, W_down, y, M, I, Dout, st);
+}
+
+static int bwd_common(bool fused, const void* x, const void* W1, const void* W_down, const void* preact,
+                      const void* dy, void* dx, void* dW1, void* dW_down, void* ws, size_t ws_bytes, int64_t M,
+                      int64_t D, int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(check_dims(M, D, I, Dout));
+  if (missing(x, M * D) || !W1 || !W_down || missing(preact, M * I) || missing(dy, M * Dout) ||
+      missing(dx, M * D) || !dW1 || !dW_down)
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned16(preact) || !aligned16(dy) ||
+      !aligned16(dx) || !aligned16(dW1) || !aligned16(dW_down) || (ws && !aligned16(ws)))
+    return SWIGLU_ERR_ALIGN;
+  const size_t need = fused ? swiglu_mlp_bwd_workspace(M, D, I, Dout) : swiglu_mlp_bwd_unfused_workspace(M, D, I, Dout);
+  if (need > 0 && (!ws || ws_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2),
+                       rng(preact, M * 2 * I * 2), rng(dy, M * Dout * 2)};
+  const Range outs[] = {rng(dx, M * D * 2), rng(dW1, D * 2 * I * 2), rng(dW_down, I * Dout * 2),
+                        rng(ws, (int64_t)need)};
+  SW_TRY(check_alias(ins, 5, outs, 4));
+  hipStream_t st = as_stream(stream);
+  char* w = (char*)ws;
+  void* gp = w;
+  void* h = w + align256((size_t)(M * 2 * I * 2));
+  if (fused) {
+    SW_TRY(step_dgrad_fused(dy, W_down, preact, gp, h, M, I, Dout, st));
+  } else {
+    void* dout = (char*)h + align256((size_t)(M * I * 2));
+    SW_TRY(step_dgrad_plain(dy, W_down, dout, M, I, Dout, st));
+    SW_TRY(step_elementwise(preact, dout, gp, h, M, I, st));
+  }
+  SW_TRY(step_dw_down(h, dy, dW_down, M, I, Dout, st));
+  SW_TRY(step_dx(gp, W1, dx, M, D, I, st));
+  return step_dw1(x, gp, dW1, M, D, I, st);
+}
+
+int swiglu_mlp_bwd(const void* x, const void* W1, const void* W_down, const void* preact, const void* dy, void* dx,
+                   void* dW1, void* dW_down, void* ws, size_t ws_bytes, int64_t M, int64_t D, int64_t I,
+                   int64_t Dout, void* stream) {
+  return bwd_common(true, x, W1, W_down, preact, dy, dx, dW1, dW_down, ws, ws_bytes, M, D, I, Dout, stream);
+}
+
+int swiglu_mlp_bwd_unfused(const void* x, const void* W1, const void* W_down, const void* preact, const void* dy,
+                           void* dx, void* dW1, void* dW_down, void* ws, size_t ws_bytes, int64_t M, int64_t D,
+                           int64_t I, int64_t Dout, void* stream) {
+  return bwd_common(false, x, W1, W_down, preact, dy, dx, dW1, dW_down, ws, ws_bytes, M, D, I, Dout, stream);
+}
+
+int swiglu_fwd_gemm1(const void* x, const void* W1, void* preact, void* h, int64_t M, int64_t D, int64_t I,
+                     void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(D));
+  SW_TRY(check_inner(I));
+  if (missing(x, M * D) || !W1 || missing(preact, M * I) || missing(h, M * I)) return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(preact) || !aligned16(h)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2)};
+  const Range outs[] = {rng(preact, M * 2 * I * 2), rng(h, M * I * 2)};
+  SW_TRY(check_alias(ins, 2, outs, 2));
+  return step_gemm1(x, W1, preact, h, M, D, I, as_stream(stream));
+}
+
+int swiglu_fwd_down(const void* h, const void* W_down, void* y, int64_t M, int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(I));
+  SW_TRY(check_inner(Dout));
+  if (missing(h, M * I) || !W_down || missing(y, M * Dout)) return SWIGLU_ERR_NULL;
+  if (!aligned16(h) || !aligned16(W_down) || !aligned16(y)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(h, M * I * 2), rng(W_down, I * Dout * 2)};
+  const Range outs[] = {rng(y, M * Dout * 2)};
+  SW_TRY(check_alias(ins, 2, outs, 1));
+  return step_down(h, W_down, y, M, I, Dout, as_stream(stream));
+}
+
+int swiglu_bwd_dgrad_fused(const void* dy, const void* W_down, const void* preact, void* grad_preact, void* h,
+                           int64_t M, int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(I));
+  SW_TRY(check_inner(Dout));
+  if (missing(dy, M * Dout) || !W_down || missing(preact, M * I) || missing(grad_preact, M * I) || missing(h, M * I))
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(dy) || !aligned16(W_down) || !aligned16(preact) || !aligned16(grad_preact) || !aligned16(h))
+    return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(dy, M * Dout * 2), rng(W_down, I * Dout * 2), rng(preact, M * 2 * I * 2)};
+  const Range outs[] = {rng(grad_preact, M * 2 * I * 2), rng(h, M * I * 2)};
+  SW_TRY(check_alias(ins, 3, outs, 2));
+  return step_dgrad_fused(dy, W_down, preact, grad_preact, h, M, I, Dout, as_stream(stream));
+}
+
+int swiglu_bwd_dgrad_plain(const void* dy, const void* W_down, void* dout, int64_t M, int64_t I, int64_t Dout,
+                           void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(I));
+  SW_TRY(check_inner(Dout));
+  if (missing(dy, M * Dout) || !W_down || missing(dout, M * I)) return SWIGLU_ERR_NULL;
+  if (!aligned16(dy) || !aligned16(W_down) || !aligned16(dout)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(dy, M * Dout * 2), rng(W_down, I * Dout * 2)};
+  const Range outs[] = {rng(dout, M * I * 2)};
+  SW_TRY(check_alias(ins, 2, outs, 1));
+  return step_dgrad_plain(dy, W_down, dout, M, I, Dout, as_stream(stream));
+}
+
+int swiglu_bwd_elementwise(const void* preact, const void* dout, void* grad_preact, void* h, int64_t M, int64_t I,
+                           void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(I));
+  if (missing(preact, M * I) || missing(dout, M * I) || missing(grad_preact, M * I) || missing(h, M * I))
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(preact) || !aligned16(dout) || !aligned16(grad_preact) || !aligned16(h)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(preact, M * 2 * I * 2), rng(dout, M * I * 2)};
+  const Range outs[] = {rng(grad_preact, M * 2 * I * 2), rng(h, M * I * 2)};
+  SW_TRY(check_alias(ins, 2, outs, 2));
+  return step_elementwise(preact, dout, grad_preact, h, M, I, as_stream(stream));
+}
+
+int swiglu_bwd_dw_down(const void* h, const void* dy, void* dW_down, int64_t M, int64_t I, int64_t Dout,
+                       void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(I));
+  SW_TRY(check_inner(Dout));
+  if (missing(h, M * I) || missing(dy, M * Dout) || !dW_down) return SWIGLU_ERR_NULL;
+  if (!aligned16(h) || !aligned16(dy) || !aligned16(dW_down)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(h, M * I * 2), rng(dy, M * Dout * 2)};
+  const Range outs[] = {rng(dW_down, I * Dout * 2)};
+  SW_TRY(check_alias(ins, 2, outs, 1));
+  return step_dw_down(h, dy, dW_down, M, I, Dout, as_stream(stream));
+}
+
+int swiglu_bwd_dx(const void* grad_preact, const void* W1, void* dx, int64_t M, int64_t D, int64_t I, void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(D));
+  SW_TRY(check_inner(I));
+  if (missing(grad_preact, M * I) || !W1 || missing(dx, M * D)) return SWIGLU_ERR_NULL;
+  if (!aligned16(grad_preact) || !aligned16(W1) || !aligned16(dx)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(grad_preact, M * 2 * I * 2), rng(W1, D * 2 * I * 2)};
+  const Range outs[] = {rng(dx, M * D * 2)};
+  SW_TRY(check_alias(ins, 2, outs, 1));
+  return step_dx(grad_preact, W1, dx, M, D, I, as_stream(stream));
+}
+
+int swiglu_bwd_dw1(const void* x, const void* grad_preact, void* dW1, int64_t M, int64_t D, int64_t I, void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(D));
+  SW_TRY(check_inner(I));
+  if (missing(x, M * D) || missing(grad_preact, M * I) || !dW1) return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(grad_preact) || !aligned16(dW1)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(x, M * D * 2), rng(grad_preact, M * 2 * I * 2)};
+  const Range outs[] = {rng(dW1, D * 2 * I * 2)};
+  SW_TRY(check_alias(ins, 2, outs, 1));
+  return step_dw1(x, grad_preact, dW1, M, D, I, as_stream(stream));
+}
+
+int swiglu_act_eval(const void* g, void* sigma, void* silu, void* dsilu, int64_t n, void* stream) {
+  if (n < 0) return SWIGLU_ERR_SHAPE;
+  if (missing(g, n) || missing(sigma, n) || missing(silu, n) || missing(dsilu, n)) return SWIGLU_ERR_NULL;
+  if (((uintptr_t)g & 1u) || ((uintptr_t)sigma & 3u) || ((uintptr_t)silu & 3u) || ((uintptr_t)dsilu & 3u))
+    return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(g, n * 2)};
+  const Range outs[] = {rng(sigma, n * 4), rng(silu, n * 4), rng(dsilu, n * 4)};
+  SW_TRY(check_alias(ins, 1, outs, 3));
+  if (n == 0) return SWIGLU_OK;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  hipLaunchKernelGGL(swg::swiglu_act_eval_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     (const uint16_t*)g, (float*)sigma, (float*)silu, (float*)dsilu, n);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+/*
+ * swiglu_mlp.h -- C ABI of the MI355X (gfx950) SwiGLU MLP training step.
+ *
+ * The step (one MLP block, no bias):
+ *   forward   preact = x . W1 = [left | gate]        [M,2I]
+ *             h      = left * silu(gate)             [M,I]   (transient)
+ *             y      = h . W_down                    [M,Dout]
+ *   backward  dout   = dy . W_down^T                 [M,I]   (never stored by
+ *                                                             the fused path)
+ *             grad_preact = [dout*silu(gate) | dout*left*silu'(gate)]
+ *             dW_down = h^T . dy,  dx = grad_preact . W1^T,  dW1 = x^T . grad_preact
+ *
+ * Sources: the note "SwiGLU MLP forward principle, backward chain and
+ * optimisation" (section 1 forward; section 2 backward steps 1-3 and the
+ * silu' forms; sections 3-4 the fused dout-GEMM epilogue), the "SwiGLU MLP
+ * Drop-H technical report" (forward/backward formulas, the saved set
+ * {x, W1, W2, preact}, h dropped after the down projection, non-inplace
+ * backward that allocates h and grad_preact), and "Lesson 24" section 11
+ * (sigma and SiLU definitions).
+ *
+ * Conventions for every entry point below:
+ *   - Tensor arguments are DEVICE pointers to bf16 values (raw 16-bit
+ *     patterns), row-major and densely packed (leading dimension = number
+ *     of columns), owned by the caller.  Each must be 16-byte aligned.
+ *   - W1 is [D, 2I]: columns [0, I) are the un-gated "left" (up) branch and
+ *     columns [I, 2I) the gate branch.  W_down is [I, Dout].
+ *   - Inputs are never written.  Outputs are overwritten (not accumulated).
+ *     No output may overlap an input or another output.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL means the default stream).  The library never allocates
+ *     device memory, never synchronises and never prints.  Device faults
+ *     surface at the caller's next synchronisation.
+ *   - Shapes: M (tokens) >= 0; D, I and Dout are positive multiples of 64.
+ *     With M == 0 the forward outputs are empty and dW1 and dW_down are
+ *     written as zeros (a sum over no tokens).
+ *   - Arithmetic: bf16 operands, fp32 accumulation and fp32 elementwise
+ *     math, bf16 round-to-nearest-even stores.
+ *   - A pointer may be NULL only when its tensor holds no elements (M == 0
+ *     for the token-indexed tensors); weights and weight gradients never.
+ *   - All argument checks run on the host before any HIP call, in this
+ *     order: shapes, null pointers, alignment, workspace size, overlap.
+ *     On any error nothing is launched and the status is returned.
+ *   - Return value: SWIGLU_OK (0) or a negative swiglu_status.  No C++
+ *     exception crosses this interface.
+ */
+#ifndef SWIGLU_MLP_H
+#define SWIGLU_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SWIGLU_OK = 0,
+  SWIGLU_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  SWIGLU_ERR_SHAPE = -2,       /* a dimension is negative or zero where > 0 needed */
+  SWIGLU_ERR_UNSUPPORTED = -3, /* D, I or Dout not a multiple of 64, or too large */
+  SWIGLU_ERR_WORKSPACE = -4,   /* ws is NULL or ws_bytes below the query result  */
+  SWIGLU_ERR_ALIAS = -5,       /* an output overlaps an input or another output  */
+  SWIGLU_ERR_HIP = -6,         /* the HIP runtime reported an error at launch    */
+  SWIGLU_ERR_ALIGN = -7        /* a tensor pointer is not 16-byte aligned        */
+} swiglu_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* swiglu_status_string(int status);
+
+/* ABI version of this header, (major << 16) | minor. */
+int swiglu_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Whole step
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace swiglu_mlp_fwd needs: the transient h [M,I].
+ * Returns 0 for invalid shapes. */
+size_t swiglu_mlp_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout);
+
+/* Bytes of device workspace swiglu_mlp_bwd needs: grad_preact [M,2I] and the
+ * recomputed h [M,I] (the drop-h report's extra backward buffers).
+ * Returns 0 for invalid shapes. */
+size_t swiglu_mlp_bwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout);
+
+/* Bytes of device workspace swiglu_mlp_bwd_unfused needs: as
+ * swiglu_mlp_bwd plus the materialised dout [M,I]. */
+size_t swiglu_mlp_bwd_unfused_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout);
+
+/* Forward of the drop-h report.  Reads x [M,D], W1 [D,2I], W_down [I,Dout];
+ * writes preact [M,2I] (the tensor the backward needs; the caller keeps it)
+ * and y [M,Dout].  h is written to `ws` and is dead once the call's work has
+ * run: the caller may reuse or free ws after the stream reaches that point.
+ * The saved set for the backward is exactly {x, W1, W_down, preact}. */
+int swiglu_mlp_fwd(const void* x, const void* W1, const void* W_down,
+                   void* preact, void* y,
+                   void* ws, size_t ws_bytes,
+                   int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
+
+/* Backward with the fused dgrad epilogue (the first note, section 4): the
+ * dout GEMM keeps each dout tile on chip, and its epilogue reads the saved
+ * [left | gate], recomputes sigma, silu and silu', and writes grad_preact and
+ * h into `ws`; then dW_down = h^T.dy, dx = grad_preact.W1^T and
+ * dW1 = x^T.grad_preact.  Reads the saved set and dy [M,Dout]; writes
+ * dx [M,D], dW1 [D,2I], dW_down [I,Dout]. */
+int swiglu_mlp_bwd(const void* x, const void* W1, const void* W_down, const void* preact,
+                   const void* dy,
+                   void* dx, void* dW1, void* dW_down,
+                   void* ws, size_t ws_bytes,
+                   int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
+
+/* The unfused baseline the first note compares against (section 4): the
+ * dout GEMM stores dout [M,I] in bf16 to `ws`, a separate elementwise kernel
+ * reads it back with preact; the rest as swiglu_mlp_bwd.  Same outputs. */
+int swiglu_mlp_bwd_unfused(const void* x, const void* W1, const void* W_down,
+                           const void* preact, const void* dy,
+                           void* dx, void* dW1, void* dW_down,
+                           void* ws, size_t ws_bytes,
+                           int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Single steps (each is one kernel launch; used by the whole-step calls
+ * above, exported for timing and for step-level parity tests)
+ * ------------------------------------------------------------------------- */
+
+/* Forward GEMM-1 with the SwiGLU epilogue (the merged gate/up GEMM of
+ * Lesson 24, sections 20-21): preact = x.W1 stored in bf16, and
+ * h = rn(left * silu(gate)) computed from the bf16-rounded left and gate.
+ * x [M,D], W1 [D,2I] -> preact [M,2I], h [M,I]. */
+int swiglu_fwd_gemm1(const void* x, const void* W1, void* preact, void* h,
+                     int64_t M, int64_t D, int64_t I, void* stream);
+
+/* Forward down GEMM: y = h . W_down.  h [M,I], W_down [I,Dout] -> y [M,Dout]. */
+int swiglu_fwd_down(const void* h, const void* W_down, void* y,
+                    int64_t M, int64_t I, int64_t Dout, void* stream);
+
+/* Fused dgrad + SwiGLU backward (the first note, sections 3-4; the drop-h
+ * report's fused h / grad_preact kernel): dout = dy . W_down^T is
+ * accumulated in fp32 and never leaves the chip; the epilogue writes
+ * grad_preact = [dout*silu(gate) | dout*left*silu'(gate)] and
+ * h = rn(left*silu(gate)).
+ * dy [M,Dout], W_down [I,Dout], preact [M,2I] -> grad_preact [M,2I], h [M,I]. */
+int swiglu_bwd_dgrad_fused(const void* dy, const void* W_down, const void* preact,
+                           void* grad_preact, void* h,
+                           int64_t M, int64_t I, int64_t Dout, void* stream);
+
+/* Baseline dgrad GEMM: dout = dy . W_down^T rounded to bf16 and stored.
+ * dy [M,Dout], W_down [I,Dout] -> dout [M,I]. */
+int swiglu_bwd_dgrad_plain(const void* dy, const void* W_down, void* dout,
+                           int64_t M, int64_t I, int64_t Dout, void* stream);
+
+/* Baseline SwiGLU-backward elementwise kernel (the drop-h report's fused
+ * h / grad_preact kernel, as a separate pass over HBM):
+ * preact [M,2I], dout [M,I] -> grad_preact [M,2I], h [M,I]. */
+int swiglu_bwd_elementwise(const void* preact, const void* dout,
+                           void* grad_preact, void* h,
+                           int64_t M, int64_t I, void* stream);
+
+/* dW_down = h^T . dy.  h [M,I], dy [M,Dout] -> dW_down [I,Dout]. */
+int swiglu_bwd_dw_down(const void* h, const void* dy, void* dW_down,
+                       int64_t M, int64_t I, int64_t Dout, void* stream);
+
+/* dx = grad_preact . W1^T.  grad_preact [M,2I], W1 [D,2I] -> dx [M,D]. */
+int swiglu_bwd_dx(const void* grad_preact, const void* W1, void* dx,
+                  int64_t M, int64_t D, int64_t I, void* stream);
+
+/* dW1 = x^T . grad_preact, one merged [D,M].[M,2I] product (the first note,
+ * section 3).  x [M,D], grad_preact [M,2I] -> dW1 [D,2I]. */
+int swiglu_bwd_dw1(const void* x, const void* grad_preact, void* dW1,
+                   int64_t M, int64_t D, int64_t I, void* stream);
+
+/* The device activation functions on n bf16 inputs g (Lesson 24,
+ * section 11; the first note, section 2, silu' forms), written as fp32:
+ * sigma(g), silu(g) = g*sigma(g), silu'(g).  Same device code as the
+ * epilogues.  n >= 0; outputs are float32 arrays of n elements; g needs
+ * only 2-byte alignment, outputs 4-byte alignment. */
+int swiglu_act_eval(const void* g, void* sigma, void* silu, void* dsilu,
+                    int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_MLP_H */

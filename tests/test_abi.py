@@ -1,0 +1,134 @@
+"""The C ABI library: it loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call.  CPU only: every call below is
+one the library must refuse, so nothing is ever launched."""
+import ctypes
+import subprocess
+
+import pytest
+
+import bwd_gemm_epilogue_amd as sw
+
+OK, NULL, SHAPE, UNSUP, WS, ALIAS, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+P = 0x10000000   # fake, 16-byte aligned "device" addresses: never dereferenced
+MB = 1 << 20
+
+
+def addr(i):
+    return P + i * (1 << 32)   # far-apart ranges: no accidental overlap
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = sw.lib()
+    names = sw.exported_names()
+    assert "swiglu_mlp_fwd" in names and "swiglu_mlp_bwd" in names
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", sw.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert f" T {n}\n" in out or out.endswith(f" T {n}"), n
+
+
+def test_status_strings():
+    L = sw.lib()
+    for s in (OK, NULL, SHAPE, UNSUP, WS, ALIAS, HIP, ALIGN):
+        assert L.swiglu_status_string(s).decode().startswith("SWIGLU_")
+    assert b"unknown" in L.swiglu_status_string(-99)
+    assert L.swiglu_abi_version() >> 16 == 1
+
+
+def test_workspace_sizes():
+    L = sw.lib()
+    M, D, I, Dout = 11136, 3584, 14336, 3584
+    assert L.swiglu_mlp_fwd_workspace(M, D, I, Dout) == M * I * 2
+    assert L.swiglu_mlp_bwd_workspace(M, D, I, Dout) == M * 2 * I * 2 + M * I * 2
+    assert L.swiglu_mlp_bwd_unfused_workspace(M, D, I, Dout) == M * 2 * I * 2 + 2 * M * I * 2
+    assert L.swiglu_mlp_fwd_workspace(-1, D, I, Dout) == 0
+    assert L.swiglu_mlp_fwd_workspace(M, 100, I, Dout) == 0
+    assert L.swiglu_mlp_bwd_workspace(0, D, I, Dout) == 0
+
+
+def _fwd(L, x=addr(0), W1=addr(1), Wd=addr(2), pre=addr(3), y=addr(4), ws=addr(5), wsb=1 << 40,
+         M=128, D=256, I=512, Dout=256):
+    return L.swiglu_mlp_fwd(x, W1, Wd, pre, y, ws, wsb, M, D, I, Dout, None)
+
+
+def _bwd(L, fn="swiglu_mlp_bwd", ptrs=None, wsb=1 << 40, M=128, D=256, I=512, Dout=256):
+    p = [addr(i) for i in range(9)] if ptrs is None else ptrs
+    return getattr(L, fn)(*p[:8], p[8], wsb, M, D, I, Dout, None)
+
+
+def test_fwd_rejects_bad_arguments():
+    L = sw.lib()
+    assert _fwd(L, x=None) == NULL
+    assert _fwd(L, y=None) == NULL
+    assert _fwd(L, M=-1) == SHAPE
+    assert _fwd(L, D=0) == SHAPE
+    assert _fwd(L, I=-64) == SHAPE
+    assert _fwd(L, D=100) == UNSUP
+    assert _fwd(L, I=96) == UNSUP
+    assert _fwd(L, Dout=32) == UNSUP
+    assert _fwd(L, I=1 << 21) == UNSUP
+    assert _fwd(L, x=addr(0) + 8) == ALIGN
+    assert _fwd(L, ws=addr(5) + 2) == ALIGN
+    assert _fwd(L, ws=None) == WS
+    assert _fwd(L, wsb=128 * 512 * 2 - 1) == WS
+    assert _fwd(L, y=addr(0)) == ALIAS                       # output on an input
+    assert _fwd(L, y=addr(3) + 64 * 1024) == ALIAS          # inside preact
+    assert _fwd(L, ws=addr(4)) == ALIAS                      # workspace on y
+
+
+def test_bwd_rejects_bad_arguments():
+    L = sw.lib()
+    for fn in ("swiglu_mlp_bwd", "swiglu_mlp_bwd_unfused"):
+        p = [addr(i) for i in range(9)]
+        for k in range(8):
+            q = list(p)
+            q[k] = None
+            assert _bwd(L, fn, q) == NULL, (fn, k)
+        assert _bwd(L, fn, M=-5) == SHAPE
+        assert _bwd(L, fn, Dout=200) == UNSUP
+        q = list(p)
+        q[5] = addr(5) + 4
+        assert _bwd(L, fn, q) == ALIGN
+        assert _bwd(L, fn, wsb=10) == WS
+        q = list(p)
+        q[8] = None
+        assert _bwd(L, fn, q) == WS
+        q = list(p)
+        q[5] = addr(3)     # dx onto preact
+        assert _bwd(L, fn, q) == ALIAS
+        q = list(p)
+        q[6] = addr(7)     # dW1 onto dW_down
+        assert _bwd(L, fn, q) == ALIAS
+        q = list(p)
+        q[8] = addr(0)     # workspace onto x
+        assert _bwd(L, fn, q) == ALIAS
+    # the unfused path needs the extra dout buffer
+    need = L.swiglu_mlp_bwd_workspace(128, 256, 512, 256)
+    assert _bwd(L, "swiglu_mlp_bwd_unfused", wsb=need) == WS
+
+
+def test_step_entry_points_reject_bad_arguments():
+    L = sw.lib()
+    a = [addr(i) for i in range(6)]
+    assert L.swiglu_fwd_gemm1(None, a[1], a[2], a[3], 128, 256, 512, None) == NULL
+    assert L.swiglu_fwd_gemm1(a[0], a[1], a[2], a[3], 128, 250, 512, None) == UNSUP
+    assert L.swiglu_fwd_gemm1(a[0], a[1], a[0], a[3], 128, 256, 512, None) == ALIAS
+    assert L.swiglu_fwd_down(a[0], a[1], a[2], -1, 512, 256, None) == SHAPE
+    assert L.swiglu_bwd_dgrad_fused(a[0], a[1], a[2], a[3], a[3], 128, 512, 256, None) == ALIAS
+    assert L.swiglu_bwd_dgrad_fused(a[0], a[1], a[2], a[3], a[4] + 1, 128, 512, 256, None) == ALIGN
+    assert L.swiglu_bwd_dgrad_plain(a[0], None, a[2], 128, 512, 256, None) == NULL
+    assert L.swiglu_bwd_elementwise(a[0], a[1], a[2], a[3], 128, 100, None) == UNSUP
+    assert L.swiglu_bwd_dw_down(a[0], a[1], a[1], 128, 512, 256, None) == ALIAS
+    assert L.swiglu_bwd_dx(a[0], a[1], a[2], 128, 0, 512, None) == SHAPE
+    assert L.swiglu_bwd_dw1(a[0], a[1], None, 128, 256, 512, None) == NULL
+    assert L.swiglu_act_eval(a[0], a[1], a[2], a[3], -1, None) == SHAPE
+    assert L.swiglu_act_eval(a[0] + 1, a[1], a[2], a[3], 16, None) == ALIGN
+    assert L.swiglu_act_eval(a[0], a[1], a[1], a[3], 16, None) == ALIAS
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sw.swiglu_fwd_down(x, torch.zeros(64, 64, dtype=torch.bfloat16))
