@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the SwiGLU MLP training step on one MI355X.
+
+One step = the whole hot path over one batch: forward GEMM-1 + SwiGLU
+epilogue, down GEMM, fused dgrad + SwiGLU-backward, dW_down, dx, dW1 (the
+kernels swiglu_mlp_fwd and swiglu_mlp_bwd launch, called step by step so that
+each kernel is timed with HIP events on the stream it runs on).
+
+Printed: one JSON line.  `value` is the fused dgrad kernel's throughput
+(2*M*Dout*I FLOPs per launch / its mean event-timed duration) in TFLOP/s;
+ms_per_step is the whole fwd+bwd step.  Extra fields: per-kernel times, the
+paired fused-vs-unfused A/B comparison of the dgrad segment (random
+interleave, medians, 3% tie rule, as the drop-h report times its variants),
+the roofline of the fused kernel and the CPU oracle timed on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload target]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import random
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SOURCES = ["bwd_gemm_epilogue_amd/csrc/gemm_core.hpp", "bwd_gemm_epilogue_amd/csrc/swiglu_mlp.hip",
+                  "bwd_gemm_epilogue_amd/csrc/swiglu_math.hpp"]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the fused dgrad kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"dgrad_fused_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="target")
+    ap.add_argument("--ab-pairs", type=int, default=40)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bwd_gemm_epilogue_amd as sw
+    from workload import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    if w.fwd_only:
+        return bench_decode(args, w)
+    M, D, I, Dout = w.M, w.D, w.I, w.Dout
+    dev = torch.device("cuda:0")
+
+    def to_dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.time()
+    xb, W1b, Wdb, dyb = make_inputs(w)
+    x, W1, Wd, dy = (to_dev(a) for a in (xb, W1b, Wdb, dyb))
+    print(f"[bench] inputs for {w.name} {M}x{D}x{I}x{Dout} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    bf = torch.bfloat16
+    preact = torch.empty((M, 2 * I), dtype=bf, device=dev)
+    h_fwd = torch.empty((M, I), dtype=bf, device=dev)
+    y = torch.empty((M, Dout), dtype=bf, device=dev)
+    gp = torch.empty((M, 2 * I), dtype=bf, device=dev)
+    h_bwd = torch.empty((M, I), dtype=bf, device=dev)
+    dout = torch.empty((M, I), dtype=bf, device=dev)
+    dx = torch.empty((M, D), dtype=bf, device=dev)
+    dW1 = torch.empty((D, 2 * I), dtype=bf, device=dev)
+    dWd = torch.empty((I, Dout), dtype=bf, device=dev)
+
+    names = ["fwd_gemm1_swiglu", "fwd_down", "bwd_dgrad_fused", "bwd_dw_down", "bwd_dx", "bwd_dw1"]
+    calls = [
+        lambda: sw.swiglu_fwd_gemm1(x, W1, preact, h_fwd),
+        lambda: sw.swiglu_fwd_down(h_fwd, Wd, y),
+        lambda: sw.swiglu_bwd_dgrad_fused(dy, Wd, preact, gp, h_bwd),
+        lambda: sw.swiglu_bwd_dw_down(h_bwd, dy, dWd),
+        lambda: sw.swiglu_bwd_dx(gp, W1, dx),
+        lambda: sw.swiglu_bwd_dw1(x, gp, dW1),
+    ]
+    flops = {
+        "fwd_gemm1_swiglu": 4 * M * D * I, "fwd_down": 2 * M * I * Dout, "bwd_dgrad_fused": 2 * M * Dout * I,
+        "bwd_dw_down": 2 * M * I * Dout, "bwd_dx": 4 * M * D * I, "bwd_dw1": 4 * M * D * I,
+    }
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        for k, c in enumerate(calls):
+            if evs is not None:
+                evs[k].record(stream)
+            c()
+        if evs is not None:
+            evs[len(calls)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evsets = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(evsets[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = {n: [] for n in names}
+    for evs in evsets:
+        for k, n in enumerate(names):
+            per[n].append(evs[k].elapsed_time(evs[k + 1]))
+    step_ms = [evs[0].elapsed_time(evs[-1]) for evs in evsets]
+    ms = {n: float(np.mean(v)) for n, v in per.items()}
+    fwd_ms = ms["fwd_gemm1_swiglu"] + ms["fwd_down"]
+    bwd_ms = sum(ms[n] for n in names[2:])
+    b1_ms = ms["bwd_dgrad_fused"]
+    b1_tflops = flops["bwd_dgrad_fused"] / (b1_ms * 1e-3) / 1e12
+    total_flops = sum(flops.values())
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- paired A/B: fused dgrad segment vs dgrad GEMM + elementwise ----
+    ab = None
+    if args.ab_pairs > 0:
+        rnd = random.Random(1234)
+        fused_t, unfused_t = [], []
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+        def seg_fused():
+            sw.swiglu_bwd_dgrad_fused(dy, Wd, preact, gp, h_bwd)
+
+        def seg_unfused():
+            sw.swiglu_bwd_dgrad_plain(dy, Wd, dout)
+            sw.swiglu_bwd_elementwise(preact, dout, gp, h_bwd)
+
+        for _ in range(3):
+            seg_fused(); seg_unfused()
+        for _ in range(args.ab_pairs):
+            order = [("f", seg_fused), ("u", seg_unfused)]
+            rnd.shuffle(order)
+            res = {}
+            for tag, fn in order:
+                e[0].record(stream)
+                fn()
+                e[1].record(stream)
+                e[1].synchronize()
+                res[tag] = e[0].elapsed_time(e[1])
+            fused_t.append(res["f"])
+            unfused_t.append(res["u"])
+        f_med, u_med = float(np.median(fused_t)), float(np.median(unfused_t))
+        delta = float(np.median((np.array(fused_t) - np.array(unfused_t)) / np.array(unfused_t)))
+        bytes_saved = 2 * M * I * 2
+        ab = {"pairs": args.ab_pairs, "fused_ms_median": round(f_med, 4), "unfused_ms_median": round(u_med, 4),
+              "paired_delta": round(delta, 4), "verdict": "tie" if abs(delta) < 0.03 else (
+                  "fused faster" if delta < 0 else "unfused faster"),
+              "dout_hbm_bytes_avoided": bytes_saved}
+
+    # ---- roofline of the fused dgrad kernel ----
+    roofline = {"kernel": "bwd_dgrad_fused", "bound": "mfma", "achieved": round(b1_tflops, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(b1_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(w.name),
+                "algorithmic_flops_per_launch": flops["bwd_dgrad_fused"],
+                "algorithmic_bytes_per_launch": 2 * (M * Dout + I * Dout + 2 * M * 2 * I + M * I)}
+
+    cpu = cpu_baseline(w, xb, W1b, Wdb, dyb, args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    out = {
+        "metric": "fused dout-GEMM+SwiGLU-bwd TFLOP/s (% MFMA peak); MLP fwd+bwd ms",
+        "value": round(b1_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} SwiGLU MLP fwd+bwd", "M": M, "D": D, "I": I, "Dout": Dout,
+                   "global_batch": M, "parallelism": "single GPU"},
+        "pct_of_mfma_peak": round(100 * b1_tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "full_ms_median": round(float(np.median(step_ms)), 4),
+        "step_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "kernels": {n: {"ms": round(ms[n], 4), "tflops": round(flops[n] / (ms[n] * 1e-3) / 1e12, 2)} for n in names},
+        "ab_fused_vs_unfused": ab,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_digest": source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("internal_api") in ("openblas", "mkl")]
+        return max(n) if n else os.cpu_count()
+    except Exception:
+        return os.cpu_count()
+
+
+def cpu_baseline(w, xb, W1b, Wdb, dyb, budget_s):
+    """The fp64 oracle of the fused dgrad step (dout = dy.W_down^T and the
+    SwiGLU backward) on a sample of token rows, scaled to TFLOP/s."""
+    import oracle
+    from workload import bf16_bits_to_f64
+    Wd = bf16_bits_to_f64(Wdb)
+    W1 = bf16_bits_to_f64(W1b)
+
+    def run(rows):
+        r = np.arange(rows)
+        pre = bf16_bits_to_f64(xb[r]) @ W1            # setup: the saved preact of those rows
+        dyr = bf16_bits_to_f64(dyb[r])
+        t = time.perf_counter()
+        dout = dyr @ Wd.T
+        oracle.swiglu_bwd_elementwise(pre, dout)
+        return time.perf_counter() - t
+
+    rows = min(64, w.M)
+    dt = run(rows)
+    rows = int(min(w.M, max(rows, rows * budget_s / max(dt, 1e-3))))
+    dt = run(rows)
+    fl = 2 * rows * w.Dout * w.I
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"fused dgrad step (dout GEMM + SwiGLU backward) of the first {rows} of {w.M} token rows, "
+                      f"fp64 numpy, {dt:.1f}s"}
+
+
+def bench_decode(args, w):
+    """Decode-shaped forward (GEMM-1 + SwiGLU epilogue, down GEMM): HBM GB/s
+    of algorithmic bytes.  Weights are rotated over enough copies to exceed
+    the 256 MB last-level cache, so every launch streams them from HBM."""
+    import torch
+    import bwd_gemm_epilogue_amd as sw
+    from workload import make_inputs
+    M, D, I, Dout = w.M, w.D, w.I, w.Dout
+    dev = torch.device("cuda:0")
+
+    def to_dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xb, W1b, Wdb, _ = make_inputs(w)
+    x = to_dev(xb)
+    copies = 3
+    W1s = [to_dev(W1b) for _ in range(copies)]
+    Wds = [to_dev(Wdb) for _ in range(copies)]
+    preact = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, Dout), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(sw.swiglu_mlp_fwd_workspace(M, D, I, Dout), dtype=torch.uint8, device=dev)
+    for k in range(args.warmup):
+        sw.swiglu_mlp_fwd(x, W1s[k % copies], Wds[k % copies], preact, y, ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        evs[k].record(stream)
+        sw.swiglu_mlp_fwd(x, W1s[k % copies], Wds[k % copies], preact, y, ws)
+    evs[-1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)]))
+    nbytes = 2 * (M * D + D * 2 * I + M * 2 * I + 2 * M * I + I * Dout + M * Dout)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "decode-shaped SwiGLU MLP forward HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name} SwiGLU MLP forward", "M": M, "D": D, "I": I, "Dout": Dout,
+                   "weight_copies_rotated": copies},
+        "roofline": {"kernel": "swiglu_mlp_fwd", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "fwd_us": round(ms * 1e3, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

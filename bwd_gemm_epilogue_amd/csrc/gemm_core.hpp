@@ -12,7 +12,8 @@
 //   A_KMAJ:  A(m,k) = A[m*lda + k]      else  A(m,k) = A[k*lda + m]
 //   B_KMAJ:  B(k,n) = B[n*ldb + k]      else  B(k,n) = B[k*ldb + n]
 //
-// Design (one workgroup per output tile, BK = 64, two LDS stages):
+// Design (one workgroup per output tile; BK-deep k-tiles in a ring of LDS
+// stages, STAGES-1 of them in flight while one is computed):
 //   * global -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging); the
 //     buffer descriptor's range check returns zeros past the end of a
 //     tensor, which masks the token tail of every GEMM;
@@ -42,9 +43,9 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 32, int STAGES_ = 4>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // one wave's output tile
@@ -54,9 +55,14 @@ struct TileCfg {
   static constexpr int SLAB_ROWS = 32 * WM;           // epilogue slab: 32 rows per wave row
   static constexpr int SLAB_LD = BN + 4;              // fp32 row pitch (+16 B breaks bank aliasing)
   static constexpr int SLAB_BYTES = SLAB_ROWS * SLAB_LD * 4;
-  static constexpr int LDS_BYTES = (2 * STAGE_BYTES > SLAB_BYTES) ? 2 * STAGE_BYTES : SLAB_BYTES;
+  static constexpr int LDS_BYTES = (STAGES * STAGE_BYTES > SLAB_BYTES) ? STAGES * STAGE_BYTES : SLAB_BYTES;
+  // direct-to-LDS load instructions each wave issues per stage (1 KB each)
+  static constexpr int LOADS_PER_STAGE = (A_BYTES + B_BYTES) / 1024 / WAVES;
+  static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+  static_assert(STAGES >= 2, "at least double buffering");
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per workgroup");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
-  static_assert((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0, "1 KB load blocks must split over waves");
+  static_assert((A_BYTES / 1024) % WAVES == 0 && (B_BYTES / 1024) % WAVES == 0, "1 KB load blocks must split over waves");
   static_assert(BM >= 64 && BN >= 64, "MN-major LDS rows need at least 8 chunks");
 };
 
@@ -74,11 +80,19 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 // LDS layouts
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz_k(int r) { return (r ^ (r >> 3)) & 7; }
+// K-major tile [rows][BK bf16]: rows of BK/8 16-byte chunks.  The chunk
+// index is XOR-ed with a function of the row so that the 8 (or 16) rows one
+// ds_read_b128 phase touches land in distinct banks.
+template <int BK>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (BK == 64) return (r ^ (r >> 3)) & 7;
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
 __device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 1; }
 
-// K-major tile [rows][64 bf16]: byte offset of 16-byte chunk c of row r
-__device__ __forceinline__ int lds_off_k(int r, int c) { return r * 128 + ((c ^ swz_k(r)) << 4); }
+// byte offset of 16-byte chunk c of row r in a K-major tile
+template <int BK>
+__device__ __forceinline__ int lds_off_k(int r, int c) { return r * (BK * 2) + ((c ^ swz_k<BK>(r)) << 4); }
 
 // MN-major tile [64][ROWS bf16]: byte offset of 16-byte chunk c of k-row k
 template <int ROWS>
@@ -86,12 +100,41 @@ __device__ __forceinline__ int lds_off_mn(int k, int c) {
   return k * (ROWS * 2) + ((c ^ swz_mn(k)) << 4);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  // dword 3 = 0x00020000: raw (untyped) buffer, 32-bit data format field as
-  // gfx9 expects; the range check then zero-fills any 16 B load at or past
-  // `bytes` (all offsets and ranges here are multiples of 16 B).
-  int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0ll : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor (V#) of a raw byte range: 48-bit base, stride 0,
+// num_records = bytes, dword 3 = 0x00020000 (32-bit data format, as gfx9
+// expects for untyped access).  The range check zero-fills any 16 B load at
+// or past `bytes` (all offsets and ranges here are multiples of 16 B).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0ll : bytes);
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+  r[2] = (int)n;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One wave-wide direct-to-LDS load: lane i's 16 B at byte offset voff of the
+// buffer land at LDS address dst + 16*i.  Issued as inline asm so that the
+// compiler's wait-count pass does not track these LDS writes: it cannot tell
+// the ring stages apart and would otherwise wait for every in-flight stage
+// before each LDS read.  Ordering is explicit instead (wait_vmcnt + barrier
+// in the main loop).  M0 (the LDS base) is saved and restored around the load.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, SWG_LDS char* dst, uint32_t voff) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(uintptr_t)dst);
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(rsrc)
+      : "memory");
 }
 
 // Element column of local MN index c (a multiple of 8) of a tile whose MN
@@ -105,23 +148,25 @@ __device__ __forceinline__ int mn_col(int c, int tile, int pair_off) {
   return tile * ROWS + c;
 }
 
-// Issue the direct-to-LDS loads of one operand tile (ROWS x 64).  One wave
+// Issue the direct-to-LDS loads of one operand tile (ROWS x BK).  One wave
 // instruction fills 1 KB of LDS, 16 B per lane in lane order; each lane picks
 // the global chunk that belongs at its LDS slot under the swizzle.
 //   K-major: rsrc is based at row `tile*ROWS` of the operand; k0 is the
 //            first k of this stage.
 //   MN-major: rsrc is based at k-row k0 of the operand.
-template <int ROWS, bool KMAJ, int WAVES>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, SWG_LDS char* dst, int64_t ld,
+template <int ROWS, int BK, bool KMAJ, int WAVES>
+__device__ __forceinline__ void load_tile(const i32x4& rsrc, SWG_LDS char* dst, int64_t ld,
                                           int k0, int tile, int pair_off, int wave, int lane) {
-  constexpr int BLOCKS = ROWS / 8;  // ROWS * 64 * 2 B / 1 KB
+  constexpr int BLOCKS = ROWS * BK * 2 / 1024;
 #pragma unroll
   for (int i = 0; i < BLOCKS / WAVES; ++i) {
     const int b = wave + i * WAVES;
     uint32_t voff;
     if constexpr (KMAJ) {
-      const int r = b * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz_k(r);
+      constexpr int CPR = BK / 8;       // 16 B chunks per row
+      constexpr int RPB = 64 / CPR;     // rows per 1 KB block
+      const int r = b * RPB + lane / CPR;
+      const int c = (lane % CPR) ^ swz_k<BK>(r);
       voff = (uint32_t)((int64_t)r * ld * 2) + (uint32_t)(k0 + c * 8) * 2u;
     } else {
       constexpr int CPR = ROWS / 8;     // 16 B chunks per k-row
@@ -131,16 +176,17 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, SWG_LDS c
       const int col = mn_col<ROWS>(c * 8, tile, pair_off);
       voff = (uint32_t)((int64_t)k * ld * 2) + (uint32_t)col * 2u;
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SWG_LDS void*)(dst + b * 1024), 16, voff, 0, 0, 0);
+    dma16(rsrc, dst + b * 1024, voff);
   }
 }
 
 // 32x16 MFMA operand fragment: lane l gets row r0 + l%32 and the 8 k values
 // kk*16 + 8*(l/32) + 0..7.
+template <int BK>
 __device__ __forceinline__ bf16x8 frag_k(const SWG_LDS char* t, int r0, int kk, int lane) {
   const int r = r0 + (lane & 31);
   const int c = kk * 2 + (lane >> 5);
-  return *(const SWG_LDS bf16x8*)(t + lds_off_k(r, c));
+  return *(const SWG_LDS bf16x8*)(t + lds_off_k<BK>(r, c));
 }
 
 // Same fragment from an MN-major tile.  ds_read_b64_tr_b16 transposes within
@@ -172,10 +218,12 @@ __device__ __forceinline__ void load_frags(const SWG_LDS char* As, const SWG_LDS
                                            int wm, int wn, int lane) {
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
-    f.a[i] = A_K ? frag_k(As, wm * T::WTM + i * 32, kk, lane) : frag_mn<T::BM>(As, wm * T::WTM + i * 32, kk, lane);
+    f.a[i] = A_K ? frag_k<T::BK>(As, wm * T::WTM + i * 32, kk, lane)
+                 : frag_mn<T::BM>(As, wm * T::WTM + i * 32, kk, lane);
 #pragma unroll
   for (int j = 0; j < T::FN; ++j)
-    f.b[j] = B_K ? frag_k(Bs, wn * T::WTN + j * 32, kk, lane) : frag_mn<T::BN>(Bs, wn * T::WTN + j * 32, kk, lane);
+    f.b[j] = B_K ? frag_k<T::BK>(Bs, wn * T::WTN + j * 32, kk, lane)
+                 : frag_mn<T::BN>(Bs, wn * T::WTN + j * 32, kk, lane);
 }
 
 // LDS read instructions per fragment set (transposing reads take two)
@@ -184,39 +232,29 @@ constexpr int frag_reads() {
   return T::FM * (A_K ? 1 : 2) + T::FN * (B_K ? 1 : 2);
 }
 
-// One LDS stage (BK = 64): four k16 steps.  Fragments of step kk+1 are read
-// while the MFMAs of step kk run; sched_group_barrier pins the interleave
-// (mask 0x008 = MFMA, 0x100 = LDS read) so each LDS read is covered by MFMAs.
-template <class T, bool A_K, bool B_K>
-__device__ __forceinline__ void compute_stage(const SWG_LDS char* As, const SWG_LDS char* Bs,
-                                              f32x16 (&acc)[T::FM][T::FN], int wm, int wn, int lane) {
-  constexpr int KSTEPS = T::BK / 16;
-  constexpr int MFMAS = T::FM * T::FN;
-  constexpr int READS = frag_reads<T, A_K, B_K>();
-  Frags<T> f[2];
-  load_frags<T, A_K, B_K>(As, Bs, f[0], 0, wm, wn, lane);
+// The MFMAs of one k16 step.  sched_group_barrier spreads the READS LDS
+// reads issued just before (the next step's fragments) over these MFMAs
+// (mask 0x008 = MFMA, 0x100 = LDS read), so each read is covered by MFMA work.
+template <class T, int READS>
+__device__ __forceinline__ void mfma_step(const Frags<T>& f, f32x16 (&acc)[T::FM][T::FN]) {
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    Frags<T>& cur = f[kk & 1];
-    if (kk + 1 < KSTEPS) load_frags<T, A_K, B_K>(As, Bs, f[(kk + 1) & 1], kk + 1, wm, wn, lane);
+  for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i)
+    for (int j = 0; j < T::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  if constexpr (READS > 0) {
+    // front-load: one read after each of the first READS MFMAs, so the reads
+    // have the rest of the step to return
+    constexpr int PER = 1;
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
-    if (kk + 1 < KSTEPS) {
-      // spread the next step's READS LDS reads over this step's MFMAS MFMAs
-      constexpr int PER = (MFMAS + READS - 1) / READS;
-#pragma unroll
-      for (int r = 0; r < READS; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-      }
+    for (int r = 0; r < READS; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
     }
-    // nothing crosses a k16 step boundary: the reads issued above stay in
-    // flight under this step's MFMAs and are waited for by the next step
-    __builtin_amdgcn_sched_barrier(0);
   }
+  // nothing crosses a k16 step boundary: reads issued before these MFMAs
+  // stay in flight under them and are consumed by the next step
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // blockIdx -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
@@ -235,6 +273,14 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
   const int in_group = id - group * GROUP_M * tiles_n;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Epilogue context handed to the epilogue functors for one slab.
@@ -273,32 +319,76 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   // K-major operands: descriptors based at the tile's first row, fixed for
   // the whole K loop.  MN-major: rebased at every stage's first k-row.
   const int nk = (g.K + T::BK - 1) / T::BK;
-  __amdgpu_buffer_rsrc_t ra =
+  i32x4 ra =
       A_K ? make_rsrc(g.A + (int64_t)tm * T::BM * g.lda, ((int64_t)g.M - (int64_t)tm * T::BM) * g.lda * 2)
           : make_rsrc(g.A, 0);
-  __amdgpu_buffer_rsrc_t rb =
+  i32x4 rb =
       B_K ? make_rsrc(g.B + (int64_t)tn * T::BN * g.ldb, ((int64_t)g.N - (int64_t)tn * T::BN) * g.ldb * 2)
           : make_rsrc(g.B, 0);
 
   auto issue = [&](int kt) {
-    SWG_LDS char* st = (SWG_LDS char*)smem + (kt & 1) * T::STAGE_BYTES;
+    SWG_LDS char* st = (SWG_LDS char*)smem + (kt % T::STAGES) * T::STAGE_BYTES;
     const int k0 = kt * T::BK;
     if constexpr (!A_K) ra = make_rsrc(g.A + (int64_t)k0 * g.lda, ((int64_t)g.K - k0) * g.lda * 2);
     if constexpr (!B_K) rb = make_rsrc(g.B + (int64_t)k0 * g.ldb, ((int64_t)g.K - k0) * g.ldb * 2);
-    load_tile<T::BM, A_K, T::WAVES>(ra, st, g.lda, A_K ? k0 : 0, tm, 0, wave, lane);
-    load_tile<T::BN, B_K, T::WAVES>(rb, st + T::A_BYTES, g.ldb, B_K ? k0 : 0, tn, g.pair_off, wave, lane);
+    load_tile<T::BM, T::BK, A_K, T::WAVES>(ra, st, g.lda, A_K ? k0 : 0, tm, 0, wave, lane);
+    load_tile<T::BN, T::BK, B_K, T::WAVES>(rb, st + T::A_BYTES, g.ldb, B_K ? k0 : 0, tn, g.pair_off, wave, lane);
   };
 
-  if (nk > 0) issue(0);
+  // Software pipeline.  Global -> LDS: a ring of STAGES buffers, the loads of
+  // stage j are issued STAGES-1 stages ahead.  LDS -> registers: fragments of
+  // k16 step s+1 are read while the MFMAs of step s run, including across the
+  // stage boundary: in the last step of stage kt the wave waits for its own
+  // loads of stage kt+1, joins the barrier (after which every wave's loads of
+  // stage kt+1 are visible, and every wave has finished reading stage kt-1,
+  // whose buffer then takes the loads of stage kt+STAGES-1), and reads the
+  // first fragments of stage kt+1 under the last MFMAs of stage kt.
+  static_assert(T::STAGES >= 3, "the stage-boundary prefetch needs >= 3 stages");
+  constexpr int KS = T::BK / 16;
+  static_assert(KS % 2 == 0, "fragment double buffer parity");
+  constexpr int READS = frag_reads<T, A_K, B_K>();
+  auto stage_ptr = [&](int kt) { return (const SWG_LDS char*)smem + (kt % T::STAGES) * T::STAGE_BYTES; };
+  // wait until at most `after` stages issued after the awaited one are in flight
+  auto wait_stages = [&](int after) {
+    if (after >= 3) wait_vmcnt<3 * T::LOADS_PER_STAGE>();
+    else if (after == 2) wait_vmcnt<2 * T::LOADS_PER_STAGE>();
+    else if (after == 1) wait_vmcnt<T::LOADS_PER_STAGE>();
+    else wait_vmcnt<0>();
+  };
+  // A bare s_barrier: __syncthreads() would add a release fence that drains
+  // every outstanding LDS DMA (vmcnt(0)) and serialises the ring.  The
+  // clobber keeps the compiler from moving LDS accesses across it.
+  auto barrier = [] { asm volatile("s_barrier" ::: "memory"); };
+
+  Frags<T> f[2];
+#pragma unroll
+  for (int p = 0; p < T::STAGES - 1; ++p)
+    if (p < nk) issue(p);
+  if (nk > 0) {
+    wait_stages(min(T::STAGES - 2, nk - 1));
+    barrier();
+    load_frags<T, A_K, B_K>(stage_ptr(0), stage_ptr(0) + T::A_BYTES, f[0], 0, wm, wn, lane);
+  }
   for (int kt = 0; kt < nk; ++kt) {
-    // this stage's loads (issued one iteration ago) have landed for this
-    // wave; the barrier makes every wave's loads visible and guarantees the
-    // other stage is no longer being read
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1);
-    const SWG_LDS char* st = (const SWG_LDS char*)smem + (kt & 1) * T::STAGE_BYTES;
-    compute_stage<T, A_K, B_K>(st, st + T::A_BYTES, acc, wm, wn, lane);
+    const SWG_LDS char* st = stage_ptr(kt);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const SWG_LDS char* src = st;
+      if (s + 1 == KS) {
+        if (kt + 1 < nk) {
+          // stages issued after kt+1 so far: up to kt+STAGES-2
+          wait_stages(min(T::STAGES - 3, nk - 2 - kt));
+          barrier();
+          if (kt + T::STAGES - 1 < nk) issue(kt + T::STAGES - 1);
+          src = stage_ptr(kt + 1);
+        }
+      }
+      // one MFMA code path for every step (the register allocator keeps the
+      // accumulators in place); after the last stage the reads re-read the
+      // current stage and are discarded
+      load_frags<T, A_K, B_K>(src, src + T::A_BYTES, f[(s + 1) & 1], (s + 1) % KS, wm, wn, lane);
+      mfma_step<T, READS>(f[s & 1], acc);
+    }
   }
   __syncthreads();
 
