@@ -13,7 +13,7 @@
 //   B_KMAJ:  B(k,n) = B[n*ldb + k]      else  B(k,n) = B[k*ldb + n]
 //
 // Design (one workgroup per output tile; BK-deep k-tiles in a ring of LDS
-// stages, STAGES-1 of them in flight while one is computed):
+// stages, the next STAGES-1 of them in flight while one is computed):
 //   * global -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging); the
 //     buffer descriptor's range check returns zeros past the end of a
 //     tensor, which masks the token tail of every GEMM;
@@ -43,7 +43,7 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 32, int STAGES_ = 4>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int STAGES_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int WM = WM_, WN = WN_;
@@ -59,6 +59,7 @@ struct TileCfg {
   // direct-to-LDS load instructions each wave issues per stage (1 KB each)
   static constexpr int LOADS_PER_STAGE = (A_BYTES + B_BYTES) / 1024 / WAVES;
   static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+  static_assert(BM % (512 / BK) == 0 && BN % (512 / BK) == 0, "whole 1 KB blocks per tile");
   static_assert(STAGES >= 2, "at least double buffering");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per workgroup");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
@@ -80,21 +81,28 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 // LDS layouts
 // ---------------------------------------------------------------------------
-// K-major tile [rows][BK bf16]: rows of BK/8 16-byte chunks.  The chunk
-// index is XOR-ed with a function of the row so that the 8 (or 16) rows one
-// ds_read_b128 phase touches land in distinct banks.
+// LDS layouts.  Every global -> LDS copy is one wave instruction that
+// fills 1 KB of LDS, 16 B per lane in lane order, so a layout is fixed by
+// which (row, chunk) each lane loads.  With BK = 64 each instruction covers
+// whole 128 B lines (one L2 request per line; BK = 32 needed twice the
+// requests), and the MFMA fragment reads must not collide in LDS banks.
+//
+// K-major tile [rows][BK]: rows of BK/8 16-byte chunks, the chunk index
+// XOR-ed with a function of the row so that the rows one ds_read_b128 phase
+// touches land in distinct banks.  The XOR stays inside a row's 128 B line
+// (BK = 64), which the vector memory path still fetches as one request.
 template <int BK>
 __device__ __forceinline__ int swz_k(int r) {
   if constexpr (BK == 64) return (r ^ (r >> 3)) & 7;
   else return ((r >> 1) ^ (r >> 3)) & 3;
 }
-__device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 1; }
-
-// byte offset of 16-byte chunk c of row r in a K-major tile
 template <int BK>
 __device__ __forceinline__ int lds_off_k(int r, int c) { return r * (BK * 2) + ((c ^ swz_k<BK>(r)) << 4); }
 
-// MN-major tile [64][ROWS bf16]: byte offset of 16-byte chunk c of k-row k
+// MN-major tile [BK][ROWS]: k-rows of ROWS/8 chunks.  The chunk index is
+// XOR-ed with 2*(k%4) so that the four k-rows one ds_read_b64_tr_b16 group
+// reads land 32 B apart in the banks.  The XOR stays inside a 128 B line.
+__device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 1; }
 template <int ROWS>
 __device__ __forceinline__ int lds_off_mn(int k, int c) {
   return k * (ROWS * 2) + ((c ^ swz_mn(k)) << 4);
@@ -154,13 +162,10 @@ __device__ __forceinline__ int mn_col(int c, int tile, int pair_off) {
 //   K-major: rsrc is based at row `tile*ROWS` of the operand; k0 is the
 //            first k of this stage.
 //   MN-major: rsrc is based at k-row k0 of the operand.
-template <int ROWS, int BK, bool KMAJ, int WAVES>
-__device__ __forceinline__ void load_tile(const i32x4& rsrc, SWG_LDS char* dst, int64_t ld,
-                                          int k0, int tile, int pair_off, int wave, int lane) {
-  constexpr int BLOCKS = ROWS * BK * 2 / 1024;
-#pragma unroll
-  for (int i = 0; i < BLOCKS / WAVES; ++i) {
-    const int b = wave + i * WAVES;
+template <int ROWS, int BK, bool KMAJ>
+__device__ __forceinline__ void load_block(const i32x4& rsrc, SWG_LDS char* dst, int64_t ld, int k0, int tile,
+                                           int pair_off, int b, int lane) {
+  {
     uint32_t voff;
     if constexpr (KMAJ) {
       constexpr int CPR = BK / 8;       // 16 B chunks per row
@@ -232,29 +237,39 @@ constexpr int frag_reads() {
   return T::FM * (A_K ? 1 : 2) + T::FN * (B_K ? 1 : 2);
 }
 
-// The MFMAs of one k16 step.  sched_group_barrier spreads the READS LDS
-// reads issued just before (the next step's fragments) over these MFMAs
-// (mask 0x008 = MFMA, 0x100 = LDS read), so each read is covered by MFMA work.
-template <class T, int READS>
-__device__ __forceinline__ void mfma_step(const Frags<T>& f, f32x16 (&acc)[T::FM][T::FN]) {
+// Read fragment i of the next step: A fragments 0..FM-1, then B fragments.
+template <class T, bool A_K, bool B_K>
+__device__ __forceinline__ void read_frag(const SWG_LDS char* As, const SWG_LDS char* Bs, Frags<T>& f, int i,
+                                          int kk, int wm, int wn, int lane) {
+  if (i < T::FM)
+    f.a[i] = A_K ? frag_k<T::BK>(As, wm * T::WTM + i * 32, kk, lane)
+                 : frag_mn<T::BM>(As, wm * T::WTM + i * 32, kk, lane);
+  else
+    f.b[i - T::FM] = B_K ? frag_k<T::BK>(Bs, wn * T::WTN + (i - T::FM) * 32, kk, lane)
+                         : frag_mn<T::BN>(Bs, wn * T::WTN + (i - T::FM) * 32, kk, lane);
+}
+
+// One k16 step with an explicit issue order, slot by slot: the LDS read of
+// next-step fragment i, then global->LDS load i (NLOAD of them, issued only
+// in a stage's last step), then MFMA i, each slot fenced by sched_barrier(0)
+// so the compiler keeps the interleave.  Spreading the loads one per MFMA
+// keeps the vector memory queue from backing up into the wave's in-order
+// instruction stream, which would stall the MFMAs behind a burst of loads.
+template <class T, bool A_K, bool B_K, int NLOAD, class LoadFn>
+__device__ __forceinline__ void step(const SWG_LDS char* src, const Frags<T>& cur, Frags<T>& nxt, int kk_next,
+                                     f32x16 (&acc)[T::FM][T::FN], int wm, int wn, int lane, LoadFn&& ld) {
+  constexpr int NF = T::FM + T::FN, NM = T::FM * T::FN;
+  constexpr int NS = (NM > NF ? NM : NF) > NLOAD ? (NM > NF ? NM : NF) : NLOAD;
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-  if constexpr (READS > 0) {
-    // front-load: one read after each of the first READS MFMAs, so the reads
-    // have the rest of the step to return
-    constexpr int PER = 1;
-#pragma unroll
-    for (int r = 0; r < READS; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+  for (int i = 0; i < NS; ++i) {
+    if (i < NF) read_frag<T, A_K, B_K>(src, src + T::A_BYTES, nxt, i, kk_next, wm, wn, lane);
+    if (i < NLOAD) ld(i);
+    if (i < NM) {
+      const int fi = i / T::FN, fj = i % T::FN;
+      acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[fj], cur.a[fi], acc[fi][fj], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // nothing crosses a k16 step boundary: reads issued before these MFMAs
-  // stay in flight under them and are consumed by the next step
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // blockIdx -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
@@ -326,70 +341,101 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
       B_K ? make_rsrc(g.B + (int64_t)tn * T::BN * g.ldb, ((int64_t)g.N - (int64_t)tn * T::BN) * g.ldb * 2)
           : make_rsrc(g.B, 0);
 
-  auto issue = [&](int kt) {
-    SWG_LDS char* st = (SWG_LDS char*)smem + (kt % T::STAGES) * T::STAGE_BYTES;
-    const int k0 = kt * T::BK;
-    if constexpr (!A_K) ra = make_rsrc(g.A + (int64_t)k0 * g.lda, ((int64_t)g.K - k0) * g.lda * 2);
-    if constexpr (!B_K) rb = make_rsrc(g.B + (int64_t)k0 * g.ldb, ((int64_t)g.K - k0) * g.ldb * 2);
-    load_tile<T::BM, T::BK, A_K, T::WAVES>(ra, st, g.lda, A_K ? k0 : 0, tm, 0, wave, lane);
-    load_tile<T::BN, T::BK, B_K, T::WAVES>(rb, st + T::A_BYTES, g.ldb, B_K ? k0 : 0, tn, g.pair_off, wave, lane);
+  // One stage's loads: LA 1 KB blocks of A, then LB of B, per wave.  Stages
+  // past the last one load through an empty descriptor (zero bytes: every
+  // lane reads 0) into a buffer nobody reads again, so the issue sequence
+  // needs no branch.  `buf` is the ring slot the loads land in.
+  constexpr int LA = T::A_BYTES / 1024 / T::WAVES, LB = T::B_BYTES / 1024 / T::WAVES;
+  struct StageLoad {
+    i32x4 ra, rb;
+    SWG_LDS char* st;
+    int k0;
+  };
+  auto plan = [&](int kt, int buf) {
+    StageLoad L;
+    L.st = (SWG_LDS char*)smem + (buf % T::STAGES) * T::STAGE_BYTES;
+    const bool live = kt < nk;
+    const int k0 = live ? kt * T::BK : 0;
+    L.k0 = k0;
+    if constexpr (A_K) L.ra = live ? ra : make_rsrc(g.A, 0);
+    else L.ra = make_rsrc(g.A + (int64_t)k0 * g.lda, live ? ((int64_t)g.K - k0) * g.lda * 2 : 0);
+    if constexpr (B_K) L.rb = live ? rb : make_rsrc(g.B, 0);
+    else L.rb = make_rsrc(g.B + (int64_t)k0 * g.ldb, live ? ((int64_t)g.K - k0) * g.ldb * 2 : 0);
+    return L;
+  };
+  auto issue_one = [&](const StageLoad& L, int j) {
+    if (j < LA)
+      load_block<T::BM, T::BK, A_K>(L.ra, L.st, g.lda, A_K ? L.k0 : 0, tm, 0, wave + j * T::WAVES, lane);
+    else
+      load_block<T::BN, T::BK, B_K>(L.rb, L.st + T::A_BYTES, g.ldb, B_K ? L.k0 : 0, tn, g.pair_off,
+                                    wave + (j - LA) * T::WAVES, lane);
   };
 
-  // Software pipeline.  Global -> LDS: a ring of STAGES buffers, the loads of
-  // stage j are issued STAGES-1 stages ahead.  LDS -> registers: fragments of
-  // k16 step s+1 are read while the MFMAs of step s run, including across the
-  // stage boundary: in the last step of stage kt the wave waits for its own
-  // loads of stage kt+1, joins the barrier (after which every wave's loads of
-  // stage kt+1 are visible, and every wave has finished reading stage kt-1,
-  // whose buffer then takes the loads of stage kt+STAGES-1), and reads the
-  // first fragments of stage kt+1 under the last MFMAs of stage kt.
-  static_assert(T::STAGES >= 3, "the stage-boundary prefetch needs >= 3 stages");
+  // Software pipeline.
+  //  * Global -> LDS: a ring of STAGES buffers; stages 0..STAGES-1 are issued
+  //    up front, and stage kt+STAGES is issued into stage kt's buffer during
+  //    the last k16 step of stage kt, one load per MFMA.
+  //  * LDS -> registers: fragments of k16 step s+1 are read while the MFMAs
+  //    of step s run, across the stage boundary too.  In the last step of
+  //    stage kt each wave waits for its own loads of stage kt+1 (vmcnt) and
+  //    for its own outstanding LDS reads (lgkmcnt: the fragments of this last
+  //    step, read one step earlier), then joins the barrier.  After it, every
+  //    wave's loads of stage kt+1 are visible and nobody reads stage kt any
+  //    more, so its buffer takes stage kt+STAGES while the first fragments of
+  //    stage kt+1 are read under the last MFMAs of stage kt.
   constexpr int KS = T::BK / 16;
   static_assert(KS % 2 == 0, "fragment double buffer parity");
-  constexpr int READS = frag_reads<T, A_K, B_K>();
   auto stage_ptr = [&](int kt) { return (const SWG_LDS char*)smem + (kt % T::STAGES) * T::STAGE_BYTES; };
-  // wait until at most `after` stages issued after the awaited one are in flight
+  // wait until at most `after` whole stages of this wave's loads are in flight
   auto wait_stages = [&](int after) {
     if (after >= 3) wait_vmcnt<3 * T::LOADS_PER_STAGE>();
     else if (after == 2) wait_vmcnt<2 * T::LOADS_PER_STAGE>();
     else if (after == 1) wait_vmcnt<T::LOADS_PER_STAGE>();
     else wait_vmcnt<0>();
   };
-  // A bare s_barrier: __syncthreads() would add a release fence that drains
-  // every outstanding LDS DMA (vmcnt(0)) and serialises the ring.  The
-  // clobber keeps the compiler from moving LDS accesses across it.
-  auto barrier = [] { asm volatile("s_barrier" ::: "memory"); };
+  // A bare s_barrier after an explicit lgkmcnt(0): __syncthreads() would add
+  // a release fence that drains every outstanding LDS DMA (vmcnt(0)) and
+  // serialises the ring.  The clobber keeps the compiler from moving LDS
+  // accesses across it.
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  auto no_load = [](int) {};
 
   Frags<T> f[2];
 #pragma unroll
-  for (int p = 0; p < T::STAGES - 1; ++p)
-    if (p < nk) issue(p);
+  for (int p = 0; p < T::STAGES; ++p) {
+    const StageLoad L = plan(p, p);
+#pragma unroll
+    for (int j = 0; j < LA + LB; ++j) issue_one(L, j);
+  }
   if (nk > 0) {
-    wait_stages(min(T::STAGES - 2, nk - 1));
+    wait_stages(min(T::STAGES - 1, nk - 1));
     barrier();
     load_frags<T, A_K, B_K>(stage_ptr(0), stage_ptr(0) + T::A_BYTES, f[0], 0, wm, wn, lane);
   }
   for (int kt = 0; kt < nk; ++kt) {
     const SWG_LDS char* st = stage_ptr(kt);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const SWG_LDS char* src = st;
-      if (s + 1 == KS) {
-        if (kt + 1 < nk) {
-          // stages issued after kt+1 so far: up to kt+STAGES-2
-          wait_stages(min(T::STAGES - 3, nk - 2 - kt));
-          barrier();
-          if (kt + T::STAGES - 1 < nk) issue(kt + T::STAGES - 1);
-          src = stage_ptr(kt + 1);
-        }
-      }
-      // one MFMA code path for every step (the register allocator keeps the
-      // accumulators in place); after the last stage the reads re-read the
-      // current stage and are discarded
-      load_frags<T, A_K, B_K>(src, src + T::A_BYTES, f[(s + 1) & 1], (s + 1) % KS, wm, wn, lane);
-      mfma_step<T, READS>(f[s & 1], acc);
+    for (int s = 0; s < KS - 1; ++s)
+      step<T, A_K, B_K, 0>(st, f[s & 1], f[(s + 1) & 1], s + 1, acc, wm, wn, lane, no_load);
+    // last step: barrier, then the next stage's first fragments and the
+    // loads of stage kt+STAGES under this step's MFMAs
+    const SWG_LDS char* src = st;
+    if (kt + 1 < nk) {
+      // issued so far: stages up to kt+STAGES-1; keep those after kt+1 in flight
+      wait_stages(min(T::STAGES - 2, nk - 2 - kt));
+      barrier();
+      src = stage_ptr(kt + 1);
     }
+    // after the barrier stage kt's buffer is free; in the final iteration
+    // there is no barrier (other waves may still read stage kt), so the
+    // empty loads go to the next slot, which held stage kt+1-STAGES < kt
+    const StageLoad L = plan(kt + T::STAGES, kt + 1 < nk ? kt : kt + 1);
+    step<T, A_K, B_K, LA + LB>(src, f[(KS - 1) & 1], f[KS & 1], 0, acc, wm, wn, lane,
+                               [&](int j) { issue_one(L, j); });
   }
+  // the tail loads (empty descriptors) may still be writing dead stage
+  // buffers that the epilogue reuses
+  wait_vmcnt<0>();
   __syncthreads();
 
   // ---- epilogue: one 32-row slab per wave row at a time through LDS ----
