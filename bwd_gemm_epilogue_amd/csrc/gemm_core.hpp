@@ -12,8 +12,8 @@
 //   A_KMAJ:  A(m,k) = A[m*lda + k]      else  A(m,k) = A[k*lda + m]
 //   B_KMAJ:  B(k,n) = B[n*ldb + k]      else  B(k,n) = B[k*ldb + n]
 //
-// Design (one workgroup per output tile; BK-deep k-tiles in a ring of LDS
-// stages, the next STAGES-1 of them in flight while one is computed):
+// Design (one workgroup per output tile; BK-deep k-tiles in LDS rings of
+// three A buffers and two B buffers):
 //   * global -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging); the
 //     buffer descriptor's range check returns zeros past the end of a
 //     tensor, which masks the token tail of every GEMM;
@@ -43,9 +43,10 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int STAGES_ = 2>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int SA = 3, SB = 2;  // LDS ring depths of the A and B tiles
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // one wave's output tile
@@ -55,12 +56,12 @@ struct TileCfg {
   static constexpr int SLAB_ROWS = 32 * WM;           // epilogue slab: 32 rows per wave row
   static constexpr int SLAB_LD = BN + 4;              // fp32 row pitch (+16 B breaks bank aliasing)
   static constexpr int SLAB_BYTES = SLAB_ROWS * SLAB_LD * 4;
-  static constexpr int LDS_BYTES = (STAGES * STAGE_BYTES > SLAB_BYTES) ? STAGES * STAGE_BYTES : SLAB_BYTES;
-  // direct-to-LDS load instructions each wave issues per stage (1 KB each)
-  static constexpr int LOADS_PER_STAGE = (A_BYTES + B_BYTES) / 1024 / WAVES;
+  static constexpr int RING_BYTES = SA * A_BYTES + SB * B_BYTES;
+  static constexpr int LDS_BYTES = (RING_BYTES > SLAB_BYTES) ? RING_BYTES : SLAB_BYTES;
+  // direct-to-LDS load instructions (1 KB each) each wave issues per stage
+  static constexpr int LA = A_BYTES / 1024 / WAVES, LB = B_BYTES / 1024 / WAVES;
   static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
   static_assert(BM % (512 / BK) == 0 && BN % (512 / BK) == 0, "whole 1 KB blocks per tile");
-  static_assert(STAGES >= 2, "at least double buffering");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per workgroup");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
   static_assert((A_BYTES / 1024) % WAVES == 0 && (B_BYTES / 1024) % WAVES == 0, "1 KB load blocks must split over waves");
@@ -256,14 +257,18 @@ __device__ __forceinline__ void read_frag(const SWG_LDS char* As, const SWG_LDS 
 // keeps the vector memory queue from backing up into the wave's in-order
 // instruction stream, which would stall the MFMAs behind a burst of loads.
 template <class T, bool A_K, bool B_K, int NLOAD, class LoadFn>
-__device__ __forceinline__ void step(const SWG_LDS char* src, const Frags<T>& cur, Frags<T>& nxt, int kk_next,
+__device__ __forceinline__ void step(const SWG_LDS char* As, const SWG_LDS char* Bs, const Frags<T>& cur,
+                                     Frags<T>& nxt, int kk_next,
                                      f32x16 (&acc)[T::FM][T::FN], int wm, int wn, int lane, LoadFn&& ld) {
   constexpr int NF = T::FM + T::FN, NM = T::FM * T::FN;
   constexpr int NS = (NM > NF ? NM : NF) > NLOAD ? (NM > NF ? NM : NF) : NLOAD;
+  // load j goes into slot j*NS/NLOAD: evenly spread over the step
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    if (i < NF) read_frag<T, A_K, B_K>(src, src + T::A_BYTES, nxt, i, kk_next, wm, wn, lane);
-    if (i < NLOAD) ld(i);
+    if (i < NF) read_frag<T, A_K, B_K>(As, Bs, nxt, i, kk_next, wm, wn, lane);
+    if constexpr (NLOAD > 0) {
+      if ((i * NLOAD) % NS < NLOAD) ld(i * NLOAD / NS);
+    }
     if (i < NM) {
       const int fi = i / T::FN, fj = i % T::FN;
       acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[fj], cur.a[fi], acc[fi][fj], 0, 0, 0);
@@ -341,57 +346,44 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
       B_K ? make_rsrc(g.B + (int64_t)tn * T::BN * g.ldb, ((int64_t)g.N - (int64_t)tn * T::BN) * g.ldb * 2)
           : make_rsrc(g.B, 0);
 
-  // One stage's loads: LA 1 KB blocks of A, then LB of B, per wave.  Stages
-  // past the last one load through an empty descriptor (zero bytes: every
-  // lane reads 0) into a buffer nobody reads again, so the issue sequence
-  // needs no branch.  `buf` is the ring slot the loads land in.
-  constexpr int LA = T::A_BYTES / 1024 / T::WAVES, LB = T::B_BYTES / 1024 / T::WAVES;
-  struct StageLoad {
-    i32x4 ra, rb;
-    SWG_LDS char* st;
-    int k0;
-  };
-  auto plan = [&](int kt, int buf) {
-    StageLoad L;
-    L.st = (SWG_LDS char*)smem + (buf % T::STAGES) * T::STAGE_BYTES;
-    const bool live = kt < nk;
-    const int k0 = live ? kt * T::BK : 0;
-    L.k0 = k0;
-    if constexpr (A_K) L.ra = live ? ra : make_rsrc(g.A, 0);
-    else L.ra = make_rsrc(g.A + (int64_t)k0 * g.lda, live ? ((int64_t)g.K - k0) * g.lda * 2 : 0);
-    if constexpr (B_K) L.rb = live ? rb : make_rsrc(g.B, 0);
-    else L.rb = make_rsrc(g.B + (int64_t)k0 * g.ldb, live ? ((int64_t)g.K - k0) * g.ldb * 2 : 0);
-    return L;
-  };
-  auto issue_one = [&](const StageLoad& L, int j) {
-    if (j < LA)
-      load_block<T::BM, T::BK, A_K>(L.ra, L.st, g.lda, A_K ? L.k0 : 0, tm, 0, wave + j * T::WAVES, lane);
-    else
-      load_block<T::BN, T::BK, B_K>(L.rb, L.st + T::A_BYTES, g.ldb, B_K ? L.k0 : 0, tn, g.pair_off,
-                                    wave + (j - LA) * T::WAVES, lane);
-  };
-
   // Software pipeline.
-  //  * Global -> LDS: a ring of STAGES buffers; stages 0..STAGES-1 are issued
-  //    up front, and stage kt+STAGES is issued into stage kt's buffer during
-  //    the last k16 step of stage kt, one load per MFMA.
+  //  * Global -> LDS: ring of SA = 3 A buffers and SB = 2 B buffers (160 KB
+  //    for 256x256 tiles).  A(j) is loaded during the first two k16 steps of
+  //    stage j-2, B(j) during the last step of stage j-2 (after its barrier).
+  //    The direct-to-LDS path drains about 64 B per clock per CU: a whole
+  //    64 KB stage issued within one step fills the address FIFO, and a
+  //    blocked load stalls the MFMAs queued behind it in the wave's in-order
+  //    stream.  Split this way, no step issues more than 32 KB per CU and
+  //    every load has at least three steps to land.
   //  * LDS -> registers: fragments of k16 step s+1 are read while the MFMAs
   //    of step s run, across the stage boundary too.  In the last step of
   //    stage kt each wave waits for its own loads of stage kt+1 (vmcnt) and
-  //    for its own outstanding LDS reads (lgkmcnt: the fragments of this last
-  //    step, read one step earlier), then joins the barrier.  After it, every
-  //    wave's loads of stage kt+1 are visible and nobody reads stage kt any
-  //    more, so its buffer takes stage kt+STAGES while the first fragments of
-  //    stage kt+1 are read under the last MFMAs of stage kt.
+  //    its own outstanding LDS reads (lgkmcnt: this step's fragments, read
+  //    one step earlier) and joins the barrier.  After it every wave's loads
+  //    of stage kt+1 are visible and nobody reads stage kt any more, so B(kt)'s
+  //    buffer takes B(kt+2); A(kt)'s buffer takes A(kt+3) one stage later.
+  static_assert(T::SA == 3 && T::SB == 2, "schedule written for a 3 + 2 ring");
   constexpr int KS = T::BK / 16;
-  static_assert(KS % 2 == 0, "fragment double buffer parity");
-  auto stage_ptr = [&](int kt) { return (const SWG_LDS char*)smem + (kt % T::STAGES) * T::STAGE_BYTES; };
-  // wait until at most `after` whole stages of this wave's loads are in flight
-  auto wait_stages = [&](int after) {
-    if (after >= 3) wait_vmcnt<3 * T::LOADS_PER_STAGE>();
-    else if (after == 2) wait_vmcnt<2 * T::LOADS_PER_STAGE>();
-    else if (after == 1) wait_vmcnt<T::LOADS_PER_STAGE>();
-    else wait_vmcnt<0>();
+  static_assert(KS == 4, "A loads use steps 0 and 1, B loads step 3");
+  constexpr int LA = T::LA, LB = T::LB;
+  static_assert(LA % 2 == 0, "A loads split over two steps");
+  auto a_ptr = [&](int j) { return (SWG_LDS char*)smem + (j % 3) * T::A_BYTES; };
+  auto b_ptr = [&](int j) { return (SWG_LDS char*)smem + 3 * T::A_BYTES + (j & 1) * T::B_BYTES; };
+  // descriptors: K-major fixed, MN-major rebased at the stage's first k-row
+  auto rs_a = [&](int j) -> i32x4 {
+    if constexpr (A_K) return ra;
+    else return make_rsrc(g.A + (int64_t)j * T::BK * g.lda, ((int64_t)g.K - (int64_t)j * T::BK) * g.lda * 2);
+  };
+  auto rs_b = [&](int j) -> i32x4 {
+    if constexpr (B_K) return rb;
+    else return make_rsrc(g.B + (int64_t)j * T::BK * g.ldb, ((int64_t)g.K - (int64_t)j * T::BK) * g.ldb * 2);
+  };
+  auto load_a = [&](const i32x4& r, int j, int idx) {
+    load_block<T::BM, T::BK, A_K>(r, a_ptr(j), g.lda, A_K ? j * T::BK : 0, tm, 0, wave + idx * T::WAVES, lane);
+  };
+  auto load_b = [&](const i32x4& r, int j, int idx) {
+    load_block<T::BN, T::BK, B_K>(r, b_ptr(j), g.ldb, B_K ? j * T::BK : 0, tn, g.pair_off, wave + idx * T::WAVES,
+                                  lane);
   };
   // A bare s_barrier after an explicit lgkmcnt(0): __syncthreads() would add
   // a release fence that drains every outstanding LDS DMA (vmcnt(0)) and
@@ -400,53 +392,81 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   auto no_load = [](int) {};
 
+  // prologue, in this issue order: A0 B0 A1 B1 A2
+  typename Epi::template Prefetch<T> pf[2];
   Frags<T> f[2];
 #pragma unroll
-  for (int p = 0; p < T::STAGES; ++p) {
-    const StageLoad L = plan(p, p);
+  for (int j = 0; j < 2; ++j) {
+    if (j < nk) {
+      const i32x4 r1 = rs_a(j), r2 = rs_b(j);
 #pragma unroll
-    for (int j = 0; j < LA + LB; ++j) issue_one(L, j);
+      for (int i = 0; i < LA; ++i) load_a(r1, j, i);
+#pragma unroll
+      for (int i = 0; i < LB; ++i) load_b(r2, j, i);
+    }
+  }
+  if (2 < nk) {
+    const i32x4 r1 = rs_a(2);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) load_a(r1, 2, i);
   }
   if (nk > 0) {
-    wait_stages(min(T::STAGES - 1, nk - 1));
+    // stage 0 landed: A1 B1 A2 (when they exist) may stay in flight
+    if (nk > 2) wait_vmcnt<2 * LA + LB>();
+    else if (nk > 1) wait_vmcnt<LA + LB>();
+    else wait_vmcnt<0>();
     barrier();
-    load_frags<T, A_K, B_K>(stage_ptr(0), stage_ptr(0) + T::A_BYTES, f[0], 0, wm, wn, lane);
+    load_frags<T, A_K, B_K>(a_ptr(0), b_ptr(0), f[0], 0, wm, wn, lane);
   }
   for (int kt = 0; kt < nk; ++kt) {
-    const SWG_LDS char* st = stage_ptr(kt);
-#pragma unroll
-    for (int s = 0; s < KS - 1; ++s)
-      step<T, A_K, B_K, 0>(st, f[s & 1], f[(s + 1) & 1], s + 1, acc, wm, wn, lane, no_load);
-    // last step: barrier, then the next stage's first fragments and the
-    // loads of stage kt+STAGES under this step's MFMAs
-    const SWG_LDS char* src = st;
+    const SWG_LDS char* as = a_ptr(kt);
+    const SWG_LDS char* bs = b_ptr(kt);
+    // the epilogue's first global reads go out under the last stage's MFMAs
+    if (kt + 1 == nk) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, tm, tn, 0, g.M, g.N}, pf[0], tid);
+    // steps 0 and 1: A(kt+2), half in each (A(2) came with the prologue)
+    const bool load_a_now = kt >= 1 && kt + 2 < nk;
+    const i32x4 rA = rs_a(kt + 2);
+    step<T, A_K, B_K, LA / 2>(as, bs, f[0], f[1], 1, acc, wm, wn, lane, [&](int i) {
+      if (load_a_now) load_a(rA, kt + 2, i);
+    });
+    step<T, A_K, B_K, LA / 2>(as, bs, f[1], f[0], 2, acc, wm, wn, lane, [&](int i) {
+      if (load_a_now) load_a(rA, kt + 2, LA / 2 + i);
+    });
+    step<T, A_K, B_K, 0>(as, bs, f[0], f[1], 3, acc, wm, wn, lane, no_load);
+    // step 3: barrier, then the next stage's first fragments and B(kt+2)
+    const SWG_LDS char* nas = as;
+    const SWG_LDS char* nbs = bs;
     if (kt + 1 < nk) {
-      // issued so far: stages up to kt+STAGES-1; keep those after kt+1 in flight
-      wait_stages(min(T::STAGES - 2, nk - 2 - kt));
+      // A(kt+1) and B(kt+1) must have landed; A(kt+2), issued after them,
+      // may stay in flight
+      if (kt + 2 < nk) wait_vmcnt<LA>();
+      else wait_vmcnt<0>();
       barrier();
-      src = stage_ptr(kt + 1);
+      nas = a_ptr(kt + 1);
+      nbs = b_ptr(kt + 1);
     }
-    // after the barrier stage kt's buffer is free; in the final iteration
-    // there is no barrier (other waves may still read stage kt), so the
-    // empty loads go to the next slot, which held stage kt+1-STAGES < kt
-    const StageLoad L = plan(kt + T::STAGES, kt + 1 < nk ? kt : kt + 1);
-    step<T, A_K, B_K, LA + LB>(src, f[(KS - 1) & 1], f[KS & 1], 0, acc, wm, wn, lane,
-                               [&](int j) { issue_one(L, j); });
+    const bool load_b_now = kt + 2 < nk;
+    const i32x4 rB = rs_b(kt + 2);
+    step<T, A_K, B_K, LB>(nas, nbs, f[1], f[0], 0, acc, wm, wn, lane, [&](int i) {
+      if (load_b_now) load_b(rB, kt + 2, i);
+    });
   }
-  // the tail loads (empty descriptors) may still be writing dead stage
-  // buffers that the epilogue reuses
-  wait_vmcnt<0>();
-  __syncthreads();
+  // Every stage load has been waited for.  The only vector memory reads in
+  // flight now are the epilogue prefetches, which must stay in flight: the
+  // barriers below are bare s_barriers, not __syncthreads() (whose fence
+  // would wait for them).
+  if (nk == 0) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, tm, tn, 0, g.M, g.N}, pf[0], tid);
+  barrier();
 
-  // ---- epilogue: one 32-row slab per wave row at a time through LDS ----
+  // ---- epilogue: one 32-row slab per wave row at a time through LDS; the
+  // global reads of slab s+1 are issued before slab s is processed ----
   SWG_LDS float* slab = (SWG_LDS float*)smem;
-  typename Epi::template Prefetch<T> pf;
   SlabCtx<T> ctx{slab, tm, tn, 0, g.M, g.N};
 #pragma unroll
   for (int s = 0; s < T::FM; ++s) {
     ctx.s = s;
-    Epi::template prefetch<T>(ep, ctx, pf, tid);
-    if (s > 0) __syncthreads();
+    if (s + 1 < T::FM) Epi::template prefetch<T>(ep, SlabCtx<T>{slab, tm, tn, s + 1, g.M, g.N}, pf[(s + 1) & 1], tid);
+    if (s > 0) barrier();
     const int sr = wm * 32 + (lane & 31);
 #pragma unroll
     for (int j = 0; j < T::FN; ++j)
@@ -456,8 +476,8 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
         f32x4 v = {acc[s][j][4 * q + 0], acc[s][j][4 * q + 1], acc[s][j][4 * q + 2], acc[s][j][4 * q + 3]};
         *(SWG_LDS f32x4*)(slab + sr * T::SLAB_LD + c) = v;
       }
-    __syncthreads();
-    Epi::template apply<T>(ep, ctx, pf, tid);
+    barrier();
+    Epi::template apply<T>(ep, ctx, pf[s & 1], tid);
   }
 }
 

@@ -188,10 +188,10 @@ namespace {
 
 using namespace swg;
 
-// tile configurations: BM, BN, waves along M and N, BK, LDS stages
-typedef TileCfg<256, 256, 2, 2, 64, 2> TBig;  // 4 waves, 128x128 per wave, 2 x 64 KB LDS stages
-typedef TileCfg<128, 128, 2, 2, 64, 3> TMid;  // 4 waves, 64x64 per wave
-typedef TileCfg<64, 64, 2, 2, 64, 3> TSmall;  // 4 waves, 32x32 per wave (N % 128 != 0)
+// tile configurations: BM, BN, waves along M and N, BK
+typedef TileCfg<256, 256, 2, 2, 64> TBig;  // 4 waves, 128x128 per wave, 160 KB LDS ring
+typedef TileCfg<128, 128, 2, 2, 64> TMid;    // 4 waves, 64x64 per wave
+typedef TileCfg<64, 64, 2, 2, 64> TSmall;      // 4 waves, 32x32 per wave (N % 128 != 0)
 
 // D, I, Dout limit: keeps every in-tile byte offset of a 256-row tile below 2^31
 constexpr int64_t kMaxDim = (int64_t)1 << 20;
