@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--ab-pairs", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (1 GiB read, 1 GiB written), "
+                         "the reference for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -83,6 +86,8 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        return copy_calibration()
     w = WORKLOADS[args.workload]
     if w.fwd_only:
         return bench_decode(args, w)
@@ -261,6 +266,21 @@ def cpu_baseline(w, xb, W1b, Wdb, dyb, budget_s):
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
             "sample": f"fused dgrad step (dout GEMM + SwiGLU backward) of the first {rows} of {w.M} token rows, "
                       f"fp64 numpy, {dt:.1f}s"}
+
+
+def copy_calibration():
+    """A plain elementwise copy (bf16 -> fp16 conversion, one read and one
+    write of 2 B per element) over 512 Mi elements: 1 GiB read, 1 GiB
+    written.  Profiling its FETCH_SIZE / WRITE_SIZE gives the factor that
+    turns those counters into bytes on this machine."""
+    import torch
+    n = 512 * 1024 * 1024
+    src = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty(n, dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"elements": n, "read_bytes": 2 * n, "write_bytes": 2 * n}}), flush=True)
 
 
 def bench_decode(args, w):
