@@ -126,23 +126,29 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
   return r;
 }
 
-// One wave-wide direct-to-LDS load: lane i's 16 B at byte offset voff of the
-// buffer land at LDS address dst + 16*i.  Issued as inline asm so that the
-// compiler's wait-count pass does not track these LDS writes: it cannot tell
-// the ring stages apart and would otherwise wait for every in-flight stage
-// before each LDS read.  Ordering is explicit instead (wait_vmcnt + barrier
-// in the main loop).  M0 (the LDS base) is saved and restored around the load.
-__device__ __forceinline__ void dma16(const i32x4& rsrc, SWG_LDS char* dst, uint32_t voff) {
+// One wave-wide direct-to-LDS load: lane i's 16 B at byte offset
+// vbase + sadd of the buffer land at LDS address dst + 16*i.  Issued as
+// inline asm so that the compiler's wait-count pass does not track these LDS
+// writes: it cannot tell the ring stages apart and would otherwise wait for
+// every in-flight stage before each LDS read.  Ordering is explicit instead
+// (wait_vmcnt + barrier in the main loop).  The offset is summed inside the
+// asm so that the compiler keeps one per-lane base per swizzle class instead
+// of hoisting one VGPR per 1 KB block out of the K loop.  M0 holds the LDS
+// base; the s_nop is the one wait state the hardware needs between writing
+// M0 and an LDS DMA reading it.  M0 is a reserved register: the compiler keeps
+// no value in it across this code (it sets it right before the few
+// instructions that read it, none of which these kernels use), so it is not
+// restored.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, SWG_LDS char* dst, uint32_t vbase, uint32_t sadd) {
   const int m0 = __builtin_amdgcn_readfirstlane((int)(uintptr_t)dst);
-  int saved;
+  uint32_t voff;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "v_add_u32 %0, %1, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(voff), "s"(rsrc)
+      "buffer_load_dwordx4 %0, %4, 0 offen lds"
+      : "=&v"(voff)
+      : "v"(vbase), "s"(sadd), "s"(m0), "s"(rsrc)
       : "memory");
 }
 
@@ -157,33 +163,38 @@ __device__ __forceinline__ int mn_col(int c, int tile, int pair_off) {
   return tile * ROWS + c;
 }
 
-// Issue the direct-to-LDS loads of one operand tile (ROWS x BK).  One wave
-// instruction fills 1 KB of LDS, 16 B per lane in lane order; each lane picks
-// the global chunk that belongs at its LDS slot under the swizzle.
-//   K-major: rsrc is based at row `tile*ROWS` of the operand; k0 is the
-//            first k of this stage.
-//   MN-major: rsrc is based at k-row k0 of the operand.
-template <int ROWS, int BK, bool KMAJ>
-__device__ __forceinline__ void load_block(const i32x4& rsrc, SWG_LDS char* dst, int64_t ld, int k0, int tile,
-                                           int pair_off, int b, int lane) {
-  {
-    uint32_t voff;
-    if constexpr (KMAJ) {
-      constexpr int CPR = BK / 8;       // 16 B chunks per row
-      constexpr int RPB = 64 / CPR;     // rows per 1 KB block
-      const int r = b * RPB + lane / CPR;
-      const int c = (lane % CPR) ^ swz_k<BK>(r);
-      voff = (uint32_t)((int64_t)r * ld * 2) + (uint32_t)(k0 + c * 8) * 2u;
-    } else {
-      constexpr int CPR = ROWS / 8;     // 16 B chunks per k-row
-      constexpr int KROWS = 64 / CPR;   // k-rows per 1 KB block
-      const int k = b * KROWS + lane / CPR;
-      const int c = (lane % CPR) ^ swz_mn(k);
-      const int col = mn_col<ROWS>(c * 8, tile, pair_off);
-      voff = (uint32_t)((int64_t)k * ld * 2) + (uint32_t)col * 2u;
-    }
-    dma16(rsrc, dst + b * 1024, voff);
+// Direct-to-LDS loads of one operand tile (ROWS x BK, BK = 64).  One wave
+// instruction fills 1 KB block b of the tile's LDS image, 16 B per lane in
+// lane order; each lane picks the global chunk that belongs at its LDS slot
+// under the swizzle.  The byte offset of lane `lane` in block b splits into
+// a per-lane part that depends on b only through its swizzle class and a
+// wave-uniform part:
+//   K-major: rsrc is based at row tile*ROWS of the operand; block b holds
+//            rows 8b .. 8b+7, row 8b + lane/8 gets chunk (lane%8) ^ swz, and
+//            swz = (lane/8) ^ (b%8): class b%8, uniform part 16*b*ld + 2*k0.
+//   MN-major: rsrc is based at k-row k0 of the operand; block b holds k-rows
+//            KROWS*b .. with KROWS = 512/ROWS, and the swizzle of k-row k is
+//            2*(k%4): class b%2 when KROWS = 2, none otherwise; uniform part
+//            2*KROWS*b*ld.
+template <int ROWS, bool KMAJ>
+__device__ __forceinline__ uint32_t dma_lane_base(int64_t ld, int tile, int pair_off, int b, int lane) {
+  if constexpr (KMAJ) {
+    const int rr = lane >> 3;
+    const int c = (lane & 7) ^ rr ^ (b & 7);
+    return (uint32_t)(rr * ld * 2) + (uint32_t)(c * 16);
+  } else {
+    constexpr int CPR = ROWS / 8, KROWS = 64 / CPR;
+    const int kr = lane / CPR;
+    const int k = KROWS * b + kr;
+    const int c = (lane % CPR) ^ swz_mn(k);
+    const int col = mn_col<ROWS>(c * 8, tile, pair_off);
+    return (uint32_t)(kr * ld * 2) + (uint32_t)col * 2u;
   }
+}
+template <int ROWS, bool KMAJ>
+__device__ __forceinline__ uint32_t dma_block_add(int64_t ld, int b, int k0) {
+  if constexpr (KMAJ) return (uint32_t)(16 * b * ld) + (uint32_t)(2 * k0);
+  else return (uint32_t)(2 * (64 / (ROWS / 8)) * b * ld);
 }
 
 // 32x16 MFMA operand fragment: lane l gets row r0 + l%32 and the 8 k values
@@ -378,12 +389,21 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
     if constexpr (B_K) return rb;
     else return make_rsrc(g.B + (int64_t)j * T::BK * g.ldb, ((int64_t)g.K - (int64_t)j * T::BK) * g.ldb * 2);
   };
+  // this wave loads blocks wave + 4i; their swizzle classes alternate
+  // between those of blocks wave and wave + 4 (K-major) or are all equal
+  // (MN-major), so two per-lane bases per operand cover every block
+  static_assert(T::WAVES == 4 && T::BK == 64, "load classes worked out for 4 waves and BK = 64");
+  const uint32_t va0 = dma_lane_base<T::BM, A_K>(g.lda, tm, 0, wave, lane);
+  const uint32_t va1 = dma_lane_base<T::BM, A_K>(g.lda, tm, 0, wave + T::WAVES, lane);
+  const uint32_t vb0 = dma_lane_base<T::BN, B_K>(g.ldb, tn, g.pair_off, wave, lane);
+  const uint32_t vb1 = dma_lane_base<T::BN, B_K>(g.ldb, tn, g.pair_off, wave + T::WAVES, lane);
   auto load_a = [&](const i32x4& r, int j, int idx) {
-    load_block<T::BM, T::BK, A_K>(r, a_ptr(j), g.lda, A_K ? j * T::BK : 0, tm, 0, wave + idx * T::WAVES, lane);
+    const int b = wave + idx * T::WAVES;
+    dma16(r, a_ptr(j) + b * 1024, (idx & 1) ? va1 : va0, dma_block_add<T::BM, A_K>(g.lda, b, A_K ? j * T::BK : 0));
   };
   auto load_b = [&](const i32x4& r, int j, int idx) {
-    load_block<T::BN, T::BK, B_K>(r, b_ptr(j), g.ldb, B_K ? j * T::BK : 0, tn, g.pair_off, wave + idx * T::WAVES,
-                                  lane);
+    const int b = wave + idx * T::WAVES;
+    dma16(r, b_ptr(j) + b * 1024, (idx & 1) ? vb1 : vb0, dma_block_add<T::BN, B_K>(g.ldb, b, B_K ? j * T::BK : 0));
   };
   // A bare s_barrier after an explicit lgkmcnt(0): __syncthreads() would add
   // a release fence that drains every outstanding LDS DMA (vmcnt(0)) and
