@@ -413,7 +413,11 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   auto no_load = [](int) {};
 
   // prologue, in this issue order: A0 B0 A1 B1 A2
-  typename Epi::template Prefetch<T> pf[2];
+  // epilogue reads in flight: slab 0's during the last stage, then up to
+  // PD slabs ahead (the main loop's fragment registers are free by then)
+  constexpr int PD = Epi::kPrefetchDepth < T::FM ? Epi::kPrefetchDepth : T::FM;
+  static_assert(PD >= 1, "prefetch depth");
+  typename Epi::template Prefetch<T> pf[PD];
   Frags<T> f[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -479,13 +483,14 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   barrier();
 
   // ---- epilogue: one 32-row slab per wave row at a time through LDS; the
-  // global reads of slab s+1 are issued before slab s is processed ----
+  // global reads of slab s+PD-1 are issued before slab s is processed ----
   SWG_LDS float* slab = (SWG_LDS float*)smem;
   SlabCtx<T> ctx{slab, tm, tn, 0, g.M, g.N};
 #pragma unroll
+  for (int s = 1; s + 1 < PD; ++s) Epi::template prefetch<T>(ep, SlabCtx<T>{slab, tm, tn, s, g.M, g.N}, pf[s], tid);
+#pragma unroll
   for (int s = 0; s < T::FM; ++s) {
     ctx.s = s;
-    if (s + 1 < T::FM) Epi::template prefetch<T>(ep, SlabCtx<T>{slab, tm, tn, s + 1, g.M, g.N}, pf[(s + 1) & 1], tid);
     if (s > 0) barrier();
     const int sr = wm * 32 + (lane & 31);
 #pragma unroll
@@ -496,8 +501,11 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
         f32x4 v = {acc[s][j][4 * q + 0], acc[s][j][4 * q + 1], acc[s][j][4 * q + 2], acc[s][j][4 * q + 3]};
         *(SWG_LDS f32x4*)(slab + sr * T::SLAB_LD + c) = v;
       }
+    // after the accumulator writes, whose staging registers are then free
+    if (s + PD - 1 < T::FM && PD > 1)
+      Epi::template prefetch<T>(ep, SlabCtx<T>{slab, tm, tn, s + PD - 1, g.M, g.N}, pf[(s + PD - 1) % PD], tid);
     barrier();
-    Epi::template apply<T>(ep, ctx, pf[s & 1], tid);
+    Epi::template apply<T>(ep, ctx, pf[s % PD], tid);
   }
 }
 
@@ -505,6 +513,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
 // Plain epilogue: C = bf16(acc), row-major with leading dimension ldc.
 // ---------------------------------------------------------------------------
 struct EpiStore {
+  static constexpr int kPrefetchDepth = 1;
   struct Params {
     uint16_t* C;
     int64_t ldc;

@@ -23,6 +23,7 @@ namespace swg {
 // preact halves and h = rn(left * silu(gate)) from the rounded values.
 // ---------------------------------------------------------------------------
 struct EpiSwigluFwd {
+  static constexpr int kPrefetchDepth = 1;
   struct Params {
     uint16_t* preact;  // [M, 2I]
     uint16_t* h;       // [M, I]
@@ -71,6 +72,9 @@ struct EpiSwigluFwd {
 //   h[:, i]               = rn(left * silu(gate))
 // ---------------------------------------------------------------------------
 struct EpiSwigluBwd {
+  // three slabs of preact reads in flight: the epilogue waits on their
+  // latency otherwise
+  static constexpr int kPrefetchDepth = 3;
   struct Params {
     const uint16_t* preact;  // [M, 2I]
     uint16_t* grad_preact;   // [M, 2I]
@@ -82,31 +86,40 @@ struct EpiSwigluBwd {
     static constexpr int N = T::SLAB_ROWS * (T::BN / 8) / T::THREADS;
     u32x4 left[N], gate[N];
   };
+  // Addresses are 32-bit byte offsets from the tile's first row: a tile
+  // spans BM rows of at most 2^21 elements, well inside 2^31 bytes, and the
+  // per-item registers stay 32-bit.
   template <class T>
   __device__ static void prefetch(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
     constexpr int CPR = T::BN / 8;
+    const int I = (int)p.I;
+    const char* base = (const char*)(p.preact + (int64_t)c.tm * T::BM * 2 * p.I);
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
       const int row = c.row(sr);
-      const int64_t i0 = (int64_t)c.tn * T::BN + ch * 8;
+      const int rl = row - c.tm * T::BM;
+      const uint32_t off = (uint32_t)(rl * 2 * I + c.tn * T::BN + ch * 8) * 2u;
       if (row < c.M) {
-        const uint16_t* pr = p.preact + (int64_t)row * 2 * p.I;
-        pf.left[k] = __builtin_nontemporal_load((const u32x4*)(pr + i0));
-        pf.gate[k] = __builtin_nontemporal_load((const u32x4*)(pr + p.I + i0));
+        pf.left[k] = __builtin_nontemporal_load((const u32x4*)(base + off));
+        pf.gate[k] = __builtin_nontemporal_load((const u32x4*)(base + off + (uint32_t)I * 2u));
       }
     }
   }
   template <class T>
   __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
     constexpr int CPR = T::BN / 8;
+    const int I = (int)p.I;
+    char* gbase = (char*)(p.grad_preact + (int64_t)c.tm * T::BM * 2 * p.I);
+    char* hbase = (char*)(p.h + (int64_t)c.tm * T::BM * p.I);
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
       const int row = c.row(sr);
-      const int64_t i0 = (int64_t)c.tn * T::BN + ch * 8;
+      const int rl = row - c.tm * T::BM;
+      const int col = c.tn * T::BN + ch * 8;
       if (row < c.M) {
         const f32x8 dout = c.read8(sr, ch * 8);
         const f32x8 left = unpack8(pf.left[k]), gate = unpack8(pf.gate[k]);
@@ -118,10 +131,12 @@ struct EpiSwigluBwd {
           dg[e] = (dout[e] * left[e]) * a.dsilu;
           h[e] = left[e] * a.silu;
         }
-        uint16_t* gpr = p.grad_preact + (int64_t)row * 2 * p.I;
-        *(u32x4*)(gpr + i0) = pack8(dl);
-        *(u32x4*)(gpr + p.I + i0) = pack8(dg);
-        *(u32x4*)(p.h + (int64_t)row * p.I + i0) = pack8(h);
+        const uint32_t off = (uint32_t)(rl * 2 * I + col) * 2u;
+        const uint32_t offh = (uint32_t)(rl * I + col) * 2u;
+        // streaming stores: nothing in this kernel reads them back
+        __builtin_nontemporal_store(pack8(dl), (u32x4*)(gbase + off));
+        __builtin_nontemporal_store(pack8(dg), (u32x4*)(gbase + off + (uint32_t)I * 2u));
+        __builtin_nontemporal_store(pack8(h), (u32x4*)(hbase + offh));
       }
     }
   }
