@@ -53,9 +53,10 @@ struct EpiSwigluFwd {
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = swiglu_h(left[e], gate[e]);
         uint16_t* pr = p.preact + (int64_t)row * 2 * p.I;
-        *(u32x4*)(pr + i0) = lp;
-        *(u32x4*)(pr + p.I + i0) = gp;
-        *(u32x4*)(p.h + (int64_t)row * p.I + i0) = pack8(h);
+        // streaming stores: nothing in this kernel reads them back
+        __builtin_nontemporal_store(lp, (u32x4*)(pr + i0));
+        __builtin_nontemporal_store(gp, (u32x4*)(pr + p.I + i0));
+        __builtin_nontemporal_store(pack8(h), (u32x4*)(p.h + (int64_t)row * p.I + i0));
       }
     }
   }
