@@ -11,8 +11,15 @@
 #include <string.h>
 
 #include "gemm_core.hpp"
+#include "skinny.hpp"
 #include "swiglu_math.hpp"
 #include "swiglu_mlp.h"
+
+#define SW_TRY(expr)                  \
+  do {                                \
+    int _s = (expr);                  \
+    if (_s != SWIGLU_OK) return _s;   \
+  } while (0)
 
 namespace swg {
 
@@ -295,6 +302,65 @@ int run_gemm_auto(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb
   return run_gemm<TSmall, A_K, B_K, Epi>(A, lda, B, ldb, M, N, K, pair_off, ep, st);
 }
 
+// --- decode-shaped forward (at most 16 token rows) -------------------------
+
+// The skinny path: 1..16 rows and column counts that are whole 128-column
+// workgroups (K is a multiple of 64 for every GEMM here).
+bool skinny_fits(int64_t M, int64_t N) { return M >= 1 && M <= 16 && N % SK_BN == 0; }
+
+// Split-K factor: about two workgroups per CU of MI355X (512) with every
+// split non-empty.  stages_per_split is returned through *spp.
+int skinny_splits(int64_t N, int64_t K, int* spp) {
+  const int64_t nblk = N / SK_BN, nk = K / SK_BK;
+  int64_t S = 512 / nblk;
+  if (S < 1) S = 1;
+  if (S > nk) S = nk;
+  const int64_t per = (nk + S - 1) / S;
+  *spp = (int)per;
+  return (int)((nk + per - 1) / per);
+}
+
+bool fwd_is_skinny(int64_t M, int64_t I, int64_t Dout) { return skinny_fits(M, 2 * I) && skinny_fits(M, Dout); }
+
+size_t skinny_partial_bytes(int64_t D, int64_t I, int64_t Dout) {
+  int spp;
+  const size_t a = (size_t)skinny_splits(2 * I, D, &spp) * 16 * (size_t)(2 * I) * 4;
+  const size_t b = (size_t)skinny_splits(Dout, I, &spp) * 16 * (size_t)Dout * 4;
+  return a > b ? a : b;
+}
+
+int run_skinny(const void* X, int64_t ldx, const void* W, int64_t M, int64_t N, int64_t K, float* partial,
+               hipStream_t st, int* S_out) {
+  SkinnyArgs a;
+  a.X = (const uint16_t*)X;
+  a.W = (const uint16_t*)W;
+  a.partial = partial;
+  a.ldx = ldx;
+  a.ldw = N;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  const int S = skinny_splits(N, K, &a.stages_per_split);
+  *S_out = S;
+  hipLaunchKernelGGL(skinny_gemm_kernel, dim3((unsigned)(N / SK_BN), (unsigned)S), dim3(256), 0, st, a);
+  return launch_status();
+}
+
+int fwd_skinny(const void* x, const void* W1, const void* Wd, void* preact, void* y, void* h, float* partial,
+               int64_t M, int64_t D, int64_t I, int64_t Dout, hipStream_t st) {
+  int S;
+  SW_TRY(run_skinny(x, D, W1, M, 2 * I, D, partial, st, &S));
+  const int64_t t1 = M * (I / 8);
+  hipLaunchKernelGGL(skinny_swiglu_reduce_kernel, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, st, partial, S,
+                     (int)M, I, (uint16_t*)preact, (uint16_t*)h);
+  SW_TRY(launch_status());
+  SW_TRY(run_skinny(h, I, Wd, M, Dout, I, partial, st, &S));
+  const int64_t t2 = M * (Dout / 8);
+  hipLaunchKernelGGL(skinny_store_reduce_kernel, dim3((unsigned)((t2 + 255) / 256)), dim3(256), 0, st, partial, S,
+                     (int)M, Dout, (uint16_t*)y);
+  return launch_status();
+}
+
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
 const uint16_t* cu16(const void* p) { return (const uint16_t*)p; }
@@ -361,12 +427,6 @@ int step_dw1(const void* x, const void* gp, void* dW1, int64_t M, int64_t D, int
   return run_gemm_auto<false, false, EpiStore>(cu16(x), D, cu16(gp), 2 * I, D, 2 * I, M, 0, ep, st);
 }
 
-#define SW_TRY(expr)                  \
-  do {                                \
-    int _s = (expr);                  \
-    if (_s != SWIGLU_OK) return _s;   \
-  } while (0)
-
 }  // namespace
 
 // ===========================================================================
@@ -392,7 +452,8 @@ int swiglu_abi_version(void) { return (1 << 16) | 0; }
 
 size_t swiglu_mlp_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
   if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
-  return align256((size_t)(M * I * 2));
+  const size_t h = align256((size_t)(M * I * 2));
+  return fwd_is_skinny(M, I, Dout) ? h + skinny_partial_bytes(D, I, Dout) : h;
 }
 
 size_t swiglu_mlp_bwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
@@ -419,6 +480,9 @@ int swiglu_mlp_fwd(const void* x, const void* W1, const void* W_down, void* prea
   const Range outs[] = {rng(preact, M * 2 * I * 2), rng(y, M * Dout * 2), rng(ws, (int64_t)need)};
   SW_TRY(check_alias(ins, 3, outs, 3));
   hipStream_t st = as_stream(stream);
+  if (fwd_is_skinny(M, I, Dout))
+    return fwd_skinny(x, W1, W_down, preact, y, ws, (float*)((char*)ws + align256((size_t)(M * I * 2))), M, D, I,
+                      Dout, st);
   SW_TRY(step_gemm1(x, W1, preact, ws, M, D, I, st));
   return step_down(ws, W_down, y, M, I, Dout, st);
 }

@@ -119,6 +119,24 @@ def test_whole_step_vs_oracle(shape, fused):
     assert_close("dW_down", to_f64(dWd), ref["dW_down"])
 
 
+@pytest.mark.parametrize("shape", [(1, 256, 512, 256), (7, 512, 768, 512), (13, 320, 192, 128),
+                                   (16, 1024, 2816, 1024), (16, 192, 320, 64)])
+def test_decode_forward_vs_oracle(shape):
+    """At most 16 token rows the forward runs the split-K weight-streaming
+    path (the last shape, Dout = 64, falls back to the tiled one): preact and
+    y against the full oracle, and preact against the tiled GEMM-1."""
+    M, D, I, Dout = shape
+    _case("decode forward", shape)
+    _, (x, W1, Wd, _), (xf, W1f, Wdf, _) = _inputs(M, D, I, Dout, seed=17)
+    pre, y = sw.swiglu_mlp_fwd(x, W1, Wd)
+    pre_t, _ = sw.swiglu_fwd_gemm1(x, W1)
+    torch.cuda.synchronize()
+    P, _, Y = oracle.forward(xf, W1f, Wdf)
+    assert_close("preact", to_f64(pre), P)
+    assert_close("y", to_f64(y), Y)
+    assert_close("preact skinny vs tiled", to_f64(pre), to_f64(pre_t))
+
+
 def test_small_workload_full_oracle():
     w = WORKLOADS["small"]
     _case("small workload", w)
