@@ -308,8 +308,10 @@ int run_gemm_auto(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb
 // workgroups (K is a multiple of 64 for every GEMM here).
 bool skinny_fits(int64_t M, int64_t N) { return M >= 1 && M <= 16 && N % SK_BN == 0; }
 
-// Split-K factor: about two workgroups per CU of MI355X (512) with every
-// split non-empty.  stages_per_split is returned through *spp.
+// Split-K factor: about 512 workgroups (two per CU of MI355X; more splits
+// measured slower: more partial-sum traffic and shorter streams per
+// workgroup) with every split non-empty.  stages_per_split is returned
+// through *spp.
 int skinny_splits(int64_t N, int64_t K, int* spp) {
   const int64_t nblk = N / SK_BN, nk = K / SK_BK;
   int64_t S = 512 / nblk;
