@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import random
@@ -33,21 +34,30 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = ["bwd_gemm_epilogue_amd/csrc/gemm_core.hpp", "bwd_gemm_epilogue_amd/csrc/swiglu_mlp.hip",
-                  "bwd_gemm_epilogue_amd/csrc/swiglu_math.hpp"]
+                  "bwd_gemm_epilogue_amd/csrc/swiglu_math.hpp", "bwd_gemm_epilogue_amd/csrc/skinny.hpp"]
+
+
+def code_text(src: str) -> str:
+    """Source text without comments and whitespace runs: the digest below
+    changes with the code, not with its comments."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
 
 
 def source_digest() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the fused dgrad kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", f"dgrad_fused_{workload}_traffic.json")
+def measured_traffic(name: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (profiles/<name>_traffic.json), if it was taken on the current kernel
+    source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -198,7 +208,7 @@ def main():
     # ---- roofline of the fused dgrad kernel ----
     roofline = {"kernel": "bwd_dgrad_fused", "bound": "mfma", "achieved": round(b1_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(b1_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(w.name),
+                "traffic": measured_traffic(f"dgrad_fused_{w.name}"),
                 "algorithmic_flops_per_launch": flops["bwd_dgrad_fused"],
                 "algorithmic_bytes_per_launch": 2 * (M * Dout + I * Dout + 2 * M * 2 * I + M * I)}
 
@@ -326,7 +336,8 @@ def bench_decode(args, w):
         "config": {"workload": f"{w.name} SwiGLU MLP forward", "M": M, "D": D, "I": I, "Dout": Dout,
                    "weight_copies_rotated": copies},
         "roofline": {"kernel": "swiglu_mlp_fwd", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(f"forward_{w.name}"),
                      "algorithmic_bytes_per_launch": nbytes},
         "fwd_us": round(ms * 1e3, 2),
     }

@@ -4,7 +4,8 @@
 // With M <= 16 the forward GEMMs of the SwiGLU MLP (the merged gate/up GEMM
 // and the down GEMM of the drop-h report's forward) are weight streams: every
 // byte of W is used for only M multiply-adds, so the bound is HBM, not the
-// matrix cores.  The tiled kernel would spend 8-16x the MFMA work on padding
+// matrix cores ("Lesson 24", sections 29-30: at decode the MLP GEMMs turn
+// into GEMV-like, weight-bandwidth-bound products).  The tiled kernel would spend 8-16x the MFMA work on padding
 // rows and launch too few workgroups to keep HBM busy.  Here:
 //   * a workgroup owns 128 columns of W and one of S contiguous k-ranges
 //     (split-K), about 512 workgroups in all;
