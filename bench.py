@@ -205,6 +205,25 @@ def main():
                   "fused faster" if delta < 0 else "unfused faster"),
               "dout_hbm_bytes_avoided": bytes_saved}
 
+    # ---- save-h fallback (the drop-h report's normal MLPBlock): the fused
+    # dgrad without its h store, and what each variant keeps after the forward
+    # alternating pairs, so that both kernels see the same clock and cache state
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(10)]
+    for e in ev2:
+        e[0].record(stream)
+        sw.swiglu_bwd_dgrad_fused(dy, Wd, preact, gp, h_bwd)
+        e[1].record(stream)
+        sw.swiglu_bwd_dgrad_fused_gp(dy, Wd, preact, gp)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    full_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev2]))
+    gp_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev2]))
+    save_h = {"bwd_dgrad_gp_ms": round(gp_ms, 4), "bwd_dgrad_fused_ms_same_pairs": round(full_ms, 4),
+              "bwd_dgrad_gp_tflops": round(flops["bwd_dgrad_fused"] / (gp_ms * 1e-3) / 1e12, 2),
+              "bwd_ms": round(gp_ms + ms["bwd_dw_down"] + ms["bwd_dx"] + ms["bwd_dw1"], 4),
+              "activation_bytes_after_fwd": {"drop_h": 2 * M * 2 * I, "save_h": 2 * M * 2 * I + 2 * M * I},
+              "h_bytes_not_written_in_bwd": 2 * M * I}
+
     # ---- roofline of the fused dgrad kernel ----
     roofline = {"kernel": "bwd_dgrad_fused", "bound": "mfma", "achieved": round(b1_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(b1_tflops / PEAK_BF16_TFLOPS, 4),
@@ -235,6 +254,7 @@ def main():
         "step_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "kernels": {n: {"ms": round(ms[n], 4), "tflops": round(flops[n] / (ms[n] * 1e-3) / 1e12, 2)} for n in names},
         "ab_fused_vs_unfused": ab,
+        "save_h_variant": save_h,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_digest": source_digest(),

@@ -25,6 +25,8 @@ __all__ = [
     "swiglu_fwd_gemm1", "swiglu_fwd_down", "swiglu_bwd_dgrad_fused", "swiglu_bwd_dgrad_plain",
     "swiglu_bwd_elementwise", "swiglu_bwd_dw_down", "swiglu_bwd_dx", "swiglu_bwd_dw1",
     "swiglu_act_eval", "SwiGLUMLPFunction", "swiglu_mlp",
+    "swiglu_mlp_fwd_save_h", "swiglu_mlp_bwd_saved_h_workspace", "swiglu_mlp_bwd_saved_h",
+    "swiglu_bwd_dgrad_fused_gp", "SwiGLUMLPSaveHFunction", "swiglu_mlp_save_h",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +55,10 @@ _SIGNATURES = {
     "swiglu_bwd_dx": (ctypes.c_int, [_P] * 3 + [_I64] * 3 + [_P]),
     "swiglu_bwd_dw1": (ctypes.c_int, [_P] * 3 + [_I64] * 3 + [_P]),
     "swiglu_act_eval": (ctypes.c_int, [_P] * 4 + [_I64] + [_P]),
+    "swiglu_mlp_fwd_save_h": (ctypes.c_int, [_P] * 6 + [_I64] * 4 + [_P]),
+    "swiglu_mlp_bwd_saved_h_workspace": (_SZ, [_I64] * 4),
+    "swiglu_mlp_bwd_saved_h": (ctypes.c_int, [_P] * 9 + [_P, _SZ] + [_I64] * 4 + [_P]),
+    "swiglu_bwd_dgrad_fused_gp": (ctypes.c_int, [_P] * 4 + [_I64] * 3 + [_P]),
 }
 
 
@@ -89,6 +95,38 @@ def exported_names():
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(swiglu_[a-z0-9_]+)\s*\(", text)))
+
+
+def swiglu_mlp_fwd_save_h(x, W1, W_down, preact=None, h=None, y=None, stream=None):
+    """Save-h forward: returns (preact [M,2I], h [M,I], y [M,Dout]); h is kept."""
+    M, D, I, Dout = _dims_fwd(x, W1, W_down)
+    preact = _empty((M, 2 * I), x) if preact is None else preact
+    h = _empty((M, I), x) if h is None else h
+    y = _empty((M, Dout), x) if y is None else y
+    _check("swiglu_mlp_fwd_save_h", lib().swiglu_mlp_fwd_save_h(
+        _dev(x, "x"), _dev(W1, "W1"), _dev(W_down, "W_down"), _dev(preact, "preact", (M, 2 * I)),
+        _dev(h, "h", (M, I)), _dev(y, "y", (M, Dout)), M, D, I, Dout, _stream(x, stream)))
+    return preact, h, y
+
+
+def swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout) -> int:
+    return lib().swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout)
+
+
+def swiglu_mlp_bwd_saved_h(x, W1, W_down, preact, h, dy, dx=None, dW1=None, dW_down=None, ws=None,
+                           stream=None):
+    """Backward from the save-h saved set {x, W1, W_down, preact, h}: (dx, dW1, dW_down)."""
+    M, D, I, Dout = _dims_fwd(x, W1, W_down)
+    dx = _empty((M, D), x) if dx is None else dx
+    dW1 = _empty((D, 2 * I), x) if dW1 is None else dW1
+    dW_down = _empty((I, Dout), x) if dW_down is None else dW_down
+    ws = _ws(swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout), x, ws)
+    _check("swiglu_mlp_bwd_saved_h", lib().swiglu_mlp_bwd_saved_h(
+        _dev(x, "x"), _dev(W1, "W1"), _dev(W_down, "W_down"), _dev(preact, "preact", (M, 2 * I)),
+        _dev(h, "h", (M, I)), _dev(dy, "dy", (M, Dout)), _dev(dx, "dx", (M, D)), _dev(dW1, "dW1", (D, 2 * I)),
+        _dev(dW_down, "dW_down", (I, Dout)), ws.data_ptr(), ws.numel() * ws.element_size(),
+        M, D, I, Dout, _stream(x, stream)))
+    return dx, dW1, dW_down
 
 
 # --------------------------------------------------------------------------
@@ -234,6 +272,17 @@ def swiglu_bwd_dgrad_fused(dy, W_down, preact, grad_preact=None, h=None, stream=
     return grad_preact, h
 
 
+def swiglu_bwd_dgrad_fused_gp(dy, W_down, preact, grad_preact=None, stream=None):
+    """The save-h path's fused dgrad: grad_preact only."""
+    M, Dout = dy.shape
+    I = W_down.shape[0]
+    grad_preact = _empty((M, 2 * I), dy) if grad_preact is None else grad_preact
+    _check("swiglu_bwd_dgrad_fused_gp", lib().swiglu_bwd_dgrad_fused_gp(
+        _dev(dy, "dy"), _dev(W_down, "W_down", (I, Dout)), _dev(preact, "preact", (M, 2 * I)),
+        _dev(grad_preact, "grad_preact", (M, 2 * I)), M, I, Dout, _stream(dy, stream)))
+    return grad_preact
+
+
 def swiglu_bwd_dgrad_plain(dy, W_down, dout=None, stream=None):
     M, Dout = dy.shape
     I = W_down.shape[0]
@@ -324,3 +373,29 @@ class SwiGLUMLPFunction(torch.autograd.Function):
 
 def swiglu_mlp(x, W1, W_down):
     return SwiGLUMLPFunction.apply(x, W1, W_down)
+
+
+class SwiGLUMLPSaveHFunction(torch.autograd.Function):
+    """The drop-h report's fallback path (normal MLPBlock): the same y, but
+    the saved set is {x, W1, W_down, preact, h} and the backward does not
+    recompute h."""
+
+    @staticmethod
+    def forward(ctx, x, W1, W_down):
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        preact, h, y = swiglu_mlp_fwd_save_h(x2, W1.contiguous(), W_down.contiguous())
+        ctx.save_for_backward(x2, W1, W_down, preact, h)
+        ctx.lead = lead
+        return y.reshape(*lead, y.shape[-1])
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        x2, W1, W_down, preact, h = ctx.saved_tensors
+        dy = grad_y.reshape(-1, grad_y.shape[-1]).contiguous()
+        dx, dW1, dW_down = swiglu_mlp_bwd_saved_h(x2, W1.contiguous(), W_down.contiguous(), preact, h, dy)
+        return dx.reshape(*ctx.lead, dx.shape[-1]), dW1, dW_down
+
+
+def swiglu_mlp_save_h(x, W1, W_down):
+    return SwiGLUMLPSaveHFunction.apply(x, W1, W_down)

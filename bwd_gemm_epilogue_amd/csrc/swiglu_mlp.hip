@@ -77,9 +77,12 @@ struct EpiSwigluFwd {
 // silu and silu', and writes
 //   grad_preact[:, i]     = dout * silu(gate)
 //   grad_preact[:, I + i] = dout * left * silu'(gate)
-//   h[:, i]               = rn(left * silu(gate))
+//   h[:, i]               = rn(left * silu(gate))     (STORE_H: the drop-h
+//                           path recomputes h here; the save-h fallback of
+//                           the drop-h report kept h from the forward)
 // ---------------------------------------------------------------------------
-struct EpiSwigluBwd {
+template <bool STORE_H>
+struct EpiSwigluBwdT {
   // three slabs of preact reads in flight: the epilogue waits on their
   // latency otherwise
   static constexpr int kPrefetchDepth = 3;
@@ -120,7 +123,7 @@ struct EpiSwigluBwd {
     constexpr int CPR = T::BN / 8;
     const int I = (int)p.I;
     char* gbase = (char*)(p.grad_preact + (int64_t)c.tm * T::BM * 2 * p.I);
-    char* hbase = (char*)(p.h + (int64_t)c.tm * T::BM * p.I);
+    char* hbase = STORE_H ? (char*)(p.h + (int64_t)c.tm * T::BM * p.I) : nullptr;
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
       const int it = tid + k * T::THREADS;
@@ -144,11 +147,13 @@ struct EpiSwigluBwd {
         // streaming stores: nothing in this kernel reads them back
         __builtin_nontemporal_store(pack8(dl), (u32x4*)(gbase + off));
         __builtin_nontemporal_store(pack8(dg), (u32x4*)(gbase + off + (uint32_t)I * 2u));
-        __builtin_nontemporal_store(pack8(h), (u32x4*)(hbase + offh));
+        if constexpr (STORE_H) __builtin_nontemporal_store(pack8(h), (u32x4*)(hbase + offh));
       }
     }
   }
 };
+typedef EpiSwigluBwdT<true> EpiSwigluBwd;     // drop-h backward: grad_preact and h
+typedef EpiSwigluBwdT<false> EpiSwigluBwdGp;  // save-h backward: grad_preact only
 
 // ---------------------------------------------------------------------------
 // Baseline elementwise SwiGLU backward (the drop-h report's fused
@@ -387,6 +392,12 @@ int step_dgrad_fused(const void* dy, const void* Wd, const void* preact, void* g
   return run_gemm_auto<true, true, EpiSwigluBwd>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, 0, ep, st);
 }
 
+int step_dgrad_fused_gp(const void* dy, const void* Wd, const void* preact, void* gp, int64_t M, int64_t I,
+                        int64_t Dout, hipStream_t st) {
+  EpiSwigluBwdGp::Params ep{cu16(preact), u16(gp), nullptr, I};
+  return run_gemm_auto<true, true, EpiSwigluBwdGp>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, 0, ep, st);
+}
+
 int step_dgrad_plain(const void* dy, const void* Wd, void* dout, int64_t M, int64_t I, int64_t Dout,
                      hipStream_t st) {
   EpiStore::Params ep{u16(dout), I};
@@ -450,7 +461,7 @@ const char* swiglu_status_string(int status) {
   }
 }
 
-int swiglu_abi_version(void) { return (1 << 16) | 0; }
+int swiglu_abi_version(void) { return (1 << 16) | 1; }
 
 size_t swiglu_mlp_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
   if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
@@ -532,6 +543,66 @@ int swiglu_mlp_bwd_unfused(const void* x, const void* W1, const void* W_down, co
                            void* dx, void* dW1, void* dW_down, void* ws, size_t ws_bytes, int64_t M, int64_t D,
                            int64_t I, int64_t Dout, void* stream) {
   return bwd_common(false, x, W1, W_down, preact, dy, dx, dW1, dW_down, ws, ws_bytes, M, D, I, Dout, stream);
+}
+
+// --- save-h fallback (the drop-h report's normal MLPBlock) ------------------
+
+size_t swiglu_mlp_bwd_saved_h_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
+  if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
+  return align256((size_t)(M * 2 * I * 2));
+}
+
+int swiglu_mlp_fwd_save_h(const void* x, const void* W1, const void* W_down, void* preact, void* h, void* y,
+                          int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(check_dims(M, D, I, Dout));
+  if (missing(x, M * D) || !W1 || !W_down || missing(preact, M * I) || missing(h, M * I) || missing(y, M * Dout))
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned16(preact) || !aligned16(h) || !aligned16(y))
+    return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2)};
+  const Range outs[] = {rng(preact, M * 2 * I * 2), rng(h, M * I * 2), rng(y, M * Dout * 2)};
+  SW_TRY(check_alias(ins, 3, outs, 3));
+  hipStream_t st = as_stream(stream);
+  SW_TRY(step_gemm1(x, W1, preact, h, M, D, I, st));
+  return step_down(h, W_down, y, M, I, Dout, st);
+}
+
+int swiglu_mlp_bwd_saved_h(const void* x, const void* W1, const void* W_down, const void* preact, const void* h,
+                           const void* dy, void* dx, void* dW1, void* dW_down, void* ws, size_t ws_bytes, int64_t M,
+                           int64_t D, int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(check_dims(M, D, I, Dout));
+  if (missing(x, M * D) || !W1 || !W_down || missing(preact, M * I) || missing(h, M * I) || missing(dy, M * Dout) ||
+      missing(dx, M * D) || !dW1 || !dW_down)
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned16(preact) || !aligned16(h) ||
+      !aligned16(dy) || !aligned16(dx) || !aligned16(dW1) || !aligned16(dW_down) || (ws && !aligned16(ws)))
+    return SWIGLU_ERR_ALIGN;
+  const size_t need = swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout);
+  if (need > 0 && (!ws || ws_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, M * D * 2),          rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2),
+                       rng(preact, M * 2 * I * 2), rng(h, M * I * 2),      rng(dy, M * Dout * 2)};
+  const Range outs[] = {rng(dx, M * D * 2), rng(dW1, D * 2 * I * 2), rng(dW_down, I * Dout * 2),
+                        rng(ws, (int64_t)need)};
+  SW_TRY(check_alias(ins, 6, outs, 4));
+  hipStream_t st = as_stream(stream);
+  SW_TRY(step_dgrad_fused_gp(dy, W_down, preact, ws, M, I, Dout, st));
+  SW_TRY(step_dw_down(h, dy, dW_down, M, I, Dout, st));
+  SW_TRY(step_dx(ws, W1, dx, M, D, I, st));
+  return step_dw1(x, ws, dW1, M, D, I, st);
+}
+
+int swiglu_bwd_dgrad_fused_gp(const void* dy, const void* W_down, const void* preact, void* grad_preact, int64_t M,
+                              int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(I));
+  SW_TRY(check_inner(Dout));
+  if (missing(dy, M * Dout) || !W_down || missing(preact, M * I) || missing(grad_preact, M * I))
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(dy) || !aligned16(W_down) || !aligned16(preact) || !aligned16(grad_preact)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(dy, M * Dout * 2), rng(W_down, I * Dout * 2), rng(preact, M * 2 * I * 2)};
+  const Range outs[] = {rng(grad_preact, M * 2 * I * 2)};
+  SW_TRY(check_alias(ins, 3, outs, 1));
+  return step_dgrad_fused_gp(dy, W_down, preact, grad_preact, M, I, Dout, as_stream(stream));
 }
 
 int swiglu_fwd_gemm1(const void* x, const void* W1, void* preact, void* h, int64_t M, int64_t D, int64_t I,

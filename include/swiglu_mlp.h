@@ -67,7 +67,7 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* swiglu_status_string(int status);
 
-/* ABI version of this header, (major << 16) | minor. */
+/* ABI version of this header, (major << 16) | minor: 1.1. */
 int swiglu_abi_version(void);
 
 /* ---------------------------------------------------------------------------
@@ -119,6 +119,34 @@ int swiglu_mlp_bwd_unfused(const void* x, const void* W1, const void* W_down,
                            int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Save-h fallback (the drop-h report's "fallback path": the normal MLPBlock
+ * that keeps h; its saved-tensor table lists h as saved by the baseline).
+ * Same arithmetic as the drop-h calls; the saved set is {x, W1, W_down,
+ * preact, h}, so the backward's dgrad epilogue writes grad_preact only.
+ * ------------------------------------------------------------------------- */
+
+/* Forward that keeps h: as swiglu_mlp_fwd, but h [M,I] is written to the
+ * caller's `h` (part of the saved set) and no workspace is used (any M takes
+ * the tiled path). */
+int swiglu_mlp_fwd_save_h(const void* x, const void* W1, const void* W_down,
+                          void* preact, void* h, void* y,
+                          int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
+
+/* Bytes of device workspace swiglu_mlp_bwd_saved_h needs: grad_preact [M,2I].
+ * Returns 0 for invalid shapes. */
+size_t swiglu_mlp_bwd_saved_h_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout);
+
+/* Backward from the saved h: the fused dgrad GEMM writes grad_preact only
+ * (swiglu_bwd_dgrad_fused_gp), dW_down = h^T.dy reads the saved h, then dx
+ * and dW1 as in swiglu_mlp_bwd.  Reads x, W1, W_down, preact, h [M,I],
+ * dy; writes dx, dW1, dW_down; grad_preact goes to `ws`. */
+int swiglu_mlp_bwd_saved_h(const void* x, const void* W1, const void* W_down, const void* preact,
+                           const void* h, const void* dy,
+                           void* dx, void* dW1, void* dW_down,
+                           void* ws, size_t ws_bytes,
+                           int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Single steps (each is one kernel launch; used by the whole-step calls
  * above, exported for timing and for step-level parity tests)
  * ------------------------------------------------------------------------- */
@@ -143,6 +171,12 @@ int swiglu_fwd_down(const void* h, const void* W_down, void* y,
 int swiglu_bwd_dgrad_fused(const void* dy, const void* W_down, const void* preact,
                            void* grad_preact, void* h,
                            int64_t M, int64_t I, int64_t Dout, void* stream);
+
+/* The fused dgrad GEMM of the save-h fallback: as swiglu_bwd_dgrad_fused
+ * without the h store.  dy [M,Dout], W_down [I,Dout], preact [M,2I] ->
+ * grad_preact [M,2I]. */
+int swiglu_bwd_dgrad_fused_gp(const void* dy, const void* W_down, const void* preact,
+                              void* grad_preact, int64_t M, int64_t I, int64_t Dout, void* stream);
 
 /* Baseline dgrad GEMM: dout = dy . W_down^T rounded to bf16 and stored.
  * dy [M,Dout], W_down [I,Dout] -> dout [M,I]. */

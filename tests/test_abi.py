@@ -127,6 +127,36 @@ def test_step_entry_points_reject_bad_arguments():
     assert L.swiglu_act_eval(a[0], a[1], a[1], a[3], 16, None) == ALIAS
 
 
+def test_save_h_entry_points_reject_bad_arguments():
+    L = sw.lib()
+    a = [addr(i) for i in range(11)]
+    M, D, I, Dout = 128, 256, 512, 256
+    fwd = lambda *p: L.swiglu_mlp_fwd_save_h(*p, M, D, I, Dout, None)
+    assert fwd(*a[:6]) is not None
+    assert fwd(None, *a[1:6]) == NULL
+    assert fwd(*a[:4], None, a[5]) == NULL                  # h is required
+    assert fwd(*a[:4], a[4] + 8, a[5]) == ALIGN
+    assert fwd(*a[:4], a[3] + 64, a[5]) == ALIAS            # h inside preact
+    assert L.swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout) == M * 2 * I * 2
+    assert L.swiglu_mlp_bwd_saved_h_workspace(M, 100, I, Dout) == 0
+    bwd = lambda p, wsb=1 << 40: L.swiglu_mlp_bwd_saved_h(*p[:9], p[9], wsb, M, D, I, Dout, None)
+    p = [addr(i) for i in range(10)]
+    for k in range(9):
+        q = list(p)
+        q[k] = None
+        assert bwd(q) == NULL, k
+    assert bwd(p, wsb=10) == WS
+    q = list(p); q[9] = None
+    assert bwd(q) == WS
+    q = list(p); q[6] = addr(4)                             # dx onto the saved h
+    assert bwd(q) == ALIAS
+    q = list(p); q[9] = addr(4)                             # workspace onto the saved h
+    assert bwd(q) == ALIAS
+    assert L.swiglu_bwd_dgrad_fused_gp(a[0], a[1], a[2], a[2], M, I, Dout, None) == ALIAS
+    assert L.swiglu_bwd_dgrad_fused_gp(a[0], None, a[2], a[3], M, I, Dout, None) == NULL
+    assert L.swiglu_bwd_dgrad_fused_gp(a[0], a[1], a[2], a[3], M, 100, Dout, None) == UNSUP
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(4, 64, dtype=torch.bfloat16)

@@ -164,6 +164,46 @@ def test_fused_matches_unfused_closely():
     assert_close("grad_preact fused vs unfused", to_f64(gp_f), to_f64(gp_u), tol=1e-2)
 
 
+@pytest.mark.parametrize("shape", [(300, 512, 768, 512), (2048, 1024, 2816, 1024)])
+def test_save_h_variant(shape):
+    """The drop-h report's fallback (h saved from the forward): bitwise the
+    same outputs as the drop-h path, h equal to the backward's recompute,
+    and the oracle's gradients."""
+    M, D, I, Dout = shape
+    _case("save-h variant", shape)
+    _, (x, W1, Wd, dy), (xf, W1f, Wdf, dyf) = _inputs(M, D, I, Dout, seed=23)
+    pre, h, y = sw.swiglu_mlp_fwd_save_h(x, W1, Wd)
+    pre0, y0 = sw.swiglu_mlp_fwd(x, W1, Wd)
+    dx, dW1, dWd = sw.swiglu_mlp_bwd_saved_h(x, W1, Wd, pre, h, dy)
+    dx0, dW10, dWd0 = sw.swiglu_mlp_bwd(x, W1, Wd, pre0, dy)
+    gp_only = sw.swiglu_bwd_dgrad_fused_gp(dy, Wd, pre)
+    gp_full, h_bwd = sw.swiglu_bwd_dgrad_fused(dy, Wd, pre)
+    torch.cuda.synchronize()
+    for a, b in ((pre, pre0), (y, y0), (h, h_bwd), (gp_only, gp_full), (dx, dx0), (dW1, dW10), (dWd, dWd0)):
+        assert np.array_equal(bits(a), bits(b))
+    ref = oracle.backward(xf, W1f, Wdf, dyf)
+    assert_close("h", to_f64(h), ref["h"])
+    assert_close("dx", to_f64(dx), ref["dx"])
+    assert_close("dW1", to_f64(dW1), ref["dW1"])
+    assert_close("dW_down", to_f64(dWd), ref["dW_down"])
+
+
+def test_save_h_autograd_saves_five_tensors():
+    B, S, D, I, Dout = 2, 64, 256, 512, 256
+    _case("save-h autograd")
+    _, (x, W1, Wd, dy), _ = _inputs(B * S, D, I, Dout, seed=29)
+    grads = []
+    for fn, nsaved in ((sw.swiglu_mlp_save_h, 5), (sw.swiglu_mlp, 4)):
+        x3 = x.view(B, S, D).clone().requires_grad_(True)
+        W1r, Wdr = W1.clone().requires_grad_(True), Wd.clone().requires_grad_(True)
+        y = fn(x3, W1r, Wdr)
+        assert len(y.grad_fn.saved_tensors) == nsaved
+        y.backward(dy.view(B, S, Dout))
+        grads.append([bits(t) for t in (y.reshape(-1, Dout), x3.grad.reshape(-1, D), W1r.grad, Wdr.grad)])
+    for a, b in zip(*grads):
+        assert np.array_equal(a, b)
+
+
 def test_empty_batch():
     D, I, Dout = 256, 512, 256
     _case("M=0")
