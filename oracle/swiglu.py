@@ -153,6 +153,32 @@ def backward(x, W1, Wd, dy):
                 dx=dx, dW1=dW1, dW_down=dW_down)
 
 
+def forward_residual(x, W1, Wd):
+    """The residual MLP block Y = X + MLP(X) (Lesson 24, section 24, the
+    residual-add epilogue of the down projection); needs Dout = D.
+    Returns (preact, h, y) in fp64 with y = x + h @ W_down."""
+    x = np.asarray(x, dtype=np.float64)
+    preact, h, m = forward(x, W1, Wd)
+    if m.shape != x.shape:
+        raise ValueError("the residual block needs Dout == D")
+    return preact, h, x + m
+
+
+def backward_residual(x, W1, Wd, dy):
+    """Backward of Y = X + MLP(X): the MLP's gradients, with the identity
+    path's dy added to dx (dX = dy + grad_preact @ W1^T); dW1 and dW_down are
+    the MLP's.  Returns the same dict as backward, with y and dx of the
+    residual block."""
+    g = backward(x, W1, Wd, dy)
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    if g["y"].shape != x.shape:
+        raise ValueError("the residual block needs Dout == D")
+    g["y"] = x + g["y"]
+    g["dx"] = g["dx"] + dy
+    return g
+
+
 def sampled_forward_backward(x, W1, Wd, dy, rows, chans):
     """Exact fp64 values of the outputs at a sample of positions, for shapes
     where the full oracle is too slow.  Same definitions as ``backward``,

@@ -136,6 +136,38 @@ def test_backward_matches_finite_differences(seed):
             assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
 
 
+def _loss_residual(x, W1, Wd, dy):
+    _, _, y = oracle.forward_residual(x, W1, Wd)
+    return float(np.sum(y * dy))
+
+
+def test_residual_block_matches_finite_differences():
+    """Y = X + MLP(X) (Lesson 24, section 24): its gradients against central
+    differences of <dy, Y>, and Y - X equal to the plain block's output."""
+    rng = np.random.default_rng(3)
+    M, D, I = 4, 6, 5
+    x, W1, Wd, dy = (_rand((M, D), rng), _rand((D, 2 * I), rng, 0.7),
+                     _rand((I, D), rng, 0.5), _rand((M, D), rng))
+    g = oracle.backward_residual(x, W1, Wd, dy)
+    _, _, y_plain = oracle.forward(x, W1, Wd)
+    _, _, y_res = oracle.forward_residual(x, W1, Wd)
+    assert np.allclose(y_res - x, y_plain, rtol=0, atol=1e-14)
+    eps = 1e-6
+    for name, arr, grad in (("x", x, g["dx"]), ("W1", W1, g["dW1"]), ("Wd", Wd, g["dW_down"])):
+        for _ in range(12):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            orig = arr[idx]
+            arr[idx] = orig + eps
+            lp = _loss_residual(x, W1, Wd, dy)
+            arr[idx] = orig - eps
+            lm = _loss_residual(x, W1, Wd, dy)
+            arr[idx] = orig
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+    with pytest.raises(ValueError):
+        oracle.forward_residual(x, W1, _rand((I, D + 1), rng))
+
+
 def test_grad_preact_matches_finite_differences():
     rng = np.random.default_rng(7)
     M, I, Dout = 4, 6, 3
