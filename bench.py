@@ -224,6 +224,33 @@ def main():
               "activation_bytes_after_fwd": {"drop_h": 2 * M * 2 * I, "save_h": 2 * M * 2 * I + 2 * M * I},
               "h_bytes_not_written_in_bwd": 2 * M * I}
 
+    # ---- residual block Y = X + MLP(X): the add in the epilogues of the down
+    # GEMM (y += x) and of the dx GEMM (dx += dy), timed in alternating pairs
+    # against the same GEMMs without it; a separate add would move 3*M*D*2
+    # bytes per tensor through HBM
+    residual = None
+    if D == Dout:
+        ev3 = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(10)]
+        y_res = torch.empty((M, D), dtype=bf, device=dev)
+        dx_res = torch.empty((M, D), dtype=bf, device=dev)
+        for e in ev3:
+            e[0].record(stream)
+            sw.swiglu_fwd_down(h_fwd, Wd, y)
+            e[1].record(stream)
+            sw.swiglu_fwd_down_residual(h_fwd, Wd, x, y_res)
+            e[2].record(stream)
+            sw.swiglu_bwd_dx(gp, W1, dx)
+            e[3].record(stream)
+            sw.swiglu_bwd_dx_residual(gp, W1, dy, dx_res)
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        med = [float(np.median([e[k].elapsed_time(e[k + 1]) for e in ev3])) for k in range(4)]
+        residual = {"fwd_down_ms": round(med[0], 4), "fwd_down_residual_ms": round(med[1], 4),
+                    "bwd_dx_ms": round(med[2], 4), "bwd_dx_residual_ms": round(med[3], 4),
+                    "epilogue_add_ms": round(med[1] - med[0] + med[3] - med[2], 4),
+                    "separate_add_hbm_bytes_avoided": 2 * 3 * M * D * 2,
+                    "separate_add_ms_at_hbm_peak": round(2 * 3 * M * D * 2 / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}
+
     # ---- roofline of the fused dgrad kernel ----
     roofline = {"kernel": "bwd_dgrad_fused", "bound": "mfma", "achieved": round(b1_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(b1_tflops / PEAK_BF16_TFLOPS, 4),
@@ -255,6 +282,7 @@ def main():
         "kernels": {n: {"ms": round(ms[n], 4), "tflops": round(flops[n] / (ms[n] * 1e-3) / 1e12, 2)} for n in names},
         "ab_fused_vs_unfused": ab,
         "save_h_variant": save_h,
+        "residual_block": residual,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_digest": source_digest(),

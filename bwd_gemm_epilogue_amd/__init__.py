@@ -27,6 +27,8 @@ __all__ = [
     "swiglu_act_eval", "SwiGLUMLPFunction", "swiglu_mlp",
     "swiglu_mlp_fwd_save_h", "swiglu_mlp_bwd_saved_h_workspace", "swiglu_mlp_bwd_saved_h",
     "swiglu_bwd_dgrad_fused_gp", "SwiGLUMLPSaveHFunction", "swiglu_mlp_save_h",
+    "swiglu_mlp_fwd_residual", "swiglu_mlp_bwd_residual", "swiglu_fwd_down_residual",
+    "swiglu_bwd_dx_residual", "SwiGLUResidualMLPFunction", "swiglu_mlp_residual",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +61,10 @@ _SIGNATURES = {
     "swiglu_mlp_bwd_saved_h_workspace": (_SZ, [_I64] * 4),
     "swiglu_mlp_bwd_saved_h": (ctypes.c_int, [_P] * 9 + [_P, _SZ] + [_I64] * 4 + [_P]),
     "swiglu_bwd_dgrad_fused_gp": (ctypes.c_int, [_P] * 4 + [_I64] * 3 + [_P]),
+    "swiglu_mlp_fwd_residual": (ctypes.c_int, [_P] * 5 + [_P, _SZ] + [_I64] * 4 + [_P]),
+    "swiglu_mlp_bwd_residual": (ctypes.c_int, [_P] * 8 + [_P, _SZ] + [_I64] * 4 + [_P]),
+    "swiglu_fwd_down_residual": (ctypes.c_int, [_P] * 4 + [_I64] * 3 + [_P]),
+    "swiglu_bwd_dx_residual": (ctypes.c_int, [_P] * 4 + [_I64] * 3 + [_P]),
 }
 
 
@@ -195,17 +201,26 @@ def swiglu_mlp_bwd_unfused_workspace(M, D, I, Dout) -> int:
     return lib().swiglu_mlp_bwd_unfused_workspace(M, D, I, Dout)
 
 
-def swiglu_mlp_fwd(x, W1, W_down, preact=None, y=None, ws=None, stream=None):
-    """Returns (preact [M,2I], y [M,Dout]); h lives only in the workspace."""
+def _fwd(fn, x, W1, W_down, preact, y, ws, stream):
     M, D, I, Dout = _dims_fwd(x, W1, W_down)
     preact = _empty((M, 2 * I), x) if preact is None else preact
     y = _empty((M, Dout), x) if y is None else y
     ws = _ws(swiglu_mlp_fwd_workspace(M, D, I, Dout), x, ws)
-    _check("swiglu_mlp_fwd", lib().swiglu_mlp_fwd(
+    _check(fn, getattr(lib(), fn)(
         _dev(x, "x"), _dev(W1, "W1"), _dev(W_down, "W_down"),
         _dev(preact, "preact", (M, 2 * I)), _dev(y, "y", (M, Dout)),
         ws.data_ptr(), ws.numel() * ws.element_size(), M, D, I, Dout, _stream(x, stream)))
     return preact, y
+
+
+def swiglu_mlp_fwd(x, W1, W_down, preact=None, y=None, ws=None, stream=None):
+    """Returns (preact [M,2I], y [M,Dout]); h lives only in the workspace."""
+    return _fwd("swiglu_mlp_fwd", x, W1, W_down, preact, y, ws, stream)
+
+
+def swiglu_mlp_fwd_residual(x, W1, W_down, preact=None, y=None, ws=None, stream=None):
+    """Residual block: returns (preact [M,2I], y = x + MLP(x) [M,D]); needs Dout == D."""
+    return _fwd("swiglu_mlp_fwd_residual", x, W1, W_down, preact, y, ws, stream)
 
 
 def _bwd(fn, wsfn, x, W1, W_down, preact, dy, dx, dW1, dW_down, ws, stream):
@@ -225,6 +240,13 @@ def _bwd(fn, wsfn, x, W1, W_down, preact, dy, dx, dW1, dW_down, ws, stream):
 def swiglu_mlp_bwd(x, W1, W_down, preact, dy, dx=None, dW1=None, dW_down=None, ws=None, stream=None):
     """Fused backward from the saved set {x, W1, W_down, preact}: (dx, dW1, dW_down)."""
     return _bwd("swiglu_mlp_bwd", swiglu_mlp_bwd_workspace, x, W1, W_down, preact, dy,
+                dx, dW1, dW_down, ws, stream)
+
+
+def swiglu_mlp_bwd_residual(x, W1, W_down, preact, dy, dx=None, dW1=None, dW_down=None, ws=None,
+                            stream=None):
+    """Backward of the residual block: dx includes dy; dW1, dW_down as swiglu_mlp_bwd."""
+    return _bwd("swiglu_mlp_bwd_residual", swiglu_mlp_bwd_workspace, x, W1, W_down, preact, dy,
                 dx, dW1, dW_down, ws, stream)
 
 
@@ -256,6 +278,17 @@ def swiglu_fwd_down(h, W_down, y=None, stream=None):
     y = _empty((M, Dout), h) if y is None else y
     _check("swiglu_fwd_down", lib().swiglu_fwd_down(
         _dev(h, "h"), _dev(W_down, "W_down", (I, Dout)), _dev(y, "y", (M, Dout)), M, I, Dout,
+        _stream(h, stream)))
+    return y
+
+
+def swiglu_fwd_down_residual(h, W_down, x, y=None, stream=None):
+    """y = h.W_down + x with the add in the GEMM epilogue."""
+    M, I = h.shape
+    D = W_down.shape[1]
+    y = _empty((M, D), h) if y is None else y
+    _check("swiglu_fwd_down_residual", lib().swiglu_fwd_down_residual(
+        _dev(h, "h"), _dev(W_down, "W_down", (I, D)), _dev(x, "x", (M, D)), _dev(y, "y", (M, D)), M, I, D,
         _stream(h, stream)))
     return y
 
@@ -320,6 +353,17 @@ def swiglu_bwd_dx(grad_preact, W1, dx=None, stream=None):
     _check("swiglu_bwd_dx", lib().swiglu_bwd_dx(
         _dev(grad_preact, "grad_preact"), _dev(W1, "W1", (D, I2)), _dev(dx, "dx", (M, D)), M, D, I2 // 2,
         _stream(grad_preact, stream)))
+    return dx
+
+
+def swiglu_bwd_dx_residual(grad_preact, W1, dy, dx=None, stream=None):
+    """dx = grad_preact.W1^T + dy with the add in the GEMM epilogue."""
+    M, I2 = grad_preact.shape
+    D = W1.shape[0]
+    dx = _empty((M, D), grad_preact) if dx is None else dx
+    _check("swiglu_bwd_dx_residual", lib().swiglu_bwd_dx_residual(
+        _dev(grad_preact, "grad_preact"), _dev(W1, "W1", (D, I2)), _dev(dy, "dy", (M, D)),
+        _dev(dx, "dx", (M, D)), M, D, I2 // 2, _stream(grad_preact, stream)))
     return dx
 
 
@@ -399,3 +443,30 @@ class SwiGLUMLPSaveHFunction(torch.autograd.Function):
 
 def swiglu_mlp_save_h(x, W1, W_down):
     return SwiGLUMLPSaveHFunction.apply(x, W1, W_down)
+
+
+class SwiGLUResidualMLPFunction(torch.autograd.Function):
+    """Residual block y = x + (left * silu(gate)) @ W_down (Lesson 24,
+    section 24): the add is fused into the down GEMM's epilogue and, in the
+    backward, dy joins dx in the dx GEMM's epilogue.  Saved set as
+    SwiGLUMLPFunction."""
+
+    @staticmethod
+    def forward(ctx, x, W1, W_down):
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        preact, y = swiglu_mlp_fwd_residual(x2, W1.contiguous(), W_down.contiguous())
+        ctx.save_for_backward(x2, W1, W_down, preact)
+        ctx.lead = lead
+        return y.reshape(*lead, y.shape[-1])
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        x2, W1, W_down, preact = ctx.saved_tensors
+        dy = grad_y.reshape(-1, grad_y.shape[-1]).contiguous()
+        dx, dW1, dW_down = swiglu_mlp_bwd_residual(x2, W1.contiguous(), W_down.contiguous(), preact, dy)
+        return dx.reshape(*ctx.lead, dx.shape[-1]), dW1, dW_down
+
+
+def swiglu_mlp_residual(x, W1, W_down):
+    return SwiGLUResidualMLPFunction.apply(x, W1, W_down)

@@ -540,4 +540,52 @@ struct EpiStore {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Residual-add epilogue ("Lesson 24", section 24): C = bf16(acc + R), the
+// residual R read in the epilogue and added in fp32 before the one rounding,
+// so no intermediate GEMM output reaches HBM.  R has C's shape.
+// ---------------------------------------------------------------------------
+struct EpiStoreResidual {
+  static constexpr int kPrefetchDepth = 2;
+  struct Params {
+    uint16_t* C;
+    int64_t ldc;
+    const uint16_t* R;
+    int64_t ldr;
+  };
+  template <class T>
+  struct Prefetch {
+    static constexpr int N = T::SLAB_ROWS * (T::BN / 8) / T::THREADS;
+    u32x4 r[N];
+  };
+  template <class T>
+  __device__ static void prefetch(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
+    constexpr int CPR = T::BN / 8;
+#pragma unroll
+    for (int k = 0; k < Prefetch<T>::N; ++k) {
+      const int it = tid + k * T::THREADS;
+      const int sr = it / CPR, ch = it % CPR;
+      const int row = c.row(sr), col = c.tn * T::BN + ch * 8;
+      if (row < c.M && col < c.N) pf.r[k] = __builtin_nontemporal_load((const u32x4*)(p.R + (int64_t)row * p.ldr + col));
+    }
+  }
+  template <class T>
+  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
+    constexpr int CPR = T::BN / 8;
+#pragma unroll
+    for (int k = 0; k < Prefetch<T>::N; ++k) {
+      const int it = tid + k * T::THREADS;
+      const int sr = it / CPR, ch = it % CPR;
+      const int row = c.row(sr), col = c.tn * T::BN + ch * 8;
+      if (row < c.M && col < c.N) {
+        f32x8 v = c.read8(sr, ch * 8);
+        const f32x8 r = unpack8(pf.r[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += r[e];
+        *(u32x4*)(p.C + (int64_t)row * p.ldc + col) = pack8(v);
+      }
+    }
+  }
+};
+
 }  // namespace swg

@@ -199,9 +199,12 @@ __global__ void __launch_bounds__(256) skinny_swiglu_reduce_kernel(const float* 
   *(u32x4*)(h + (int64_t)m * I + i0) = pack8(hv);
 }
 
-// y[m, n] = rn(sum_s partial[s][m][n]).  One thread per (m, 8 columns).
+// y[m, n] = rn(sum_s partial[s][m][n] (+ res[m, n] when res is given: the
+// residual-add epilogue, added in fp32 before the one rounding)).  One thread
+// per (m, 8 columns).
 __global__ void __launch_bounds__(256) skinny_store_reduce_kernel(const float* __restrict__ partial, int S, int M,
-                                                                  int64_t N, uint16_t* __restrict__ y) {
+                                                                  int64_t N, uint16_t* __restrict__ y,
+                                                                  const uint16_t* __restrict__ res) {
   const int64_t cpr = N / 8;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= (int64_t)M * cpr) return;
@@ -229,6 +232,11 @@ __global__ void __launch_bounds__(256) skinny_store_reduce_kernel(const float* _
         }
       }
     }
+  }
+  if (res != nullptr) {
+    const f32x8 r = unpack8(*(const u32x4*)(res + (int64_t)m * N + n0));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += r[e];
   }
   *(u32x4*)(y + (int64_t)m * N + n0) = pack8(v);
 }

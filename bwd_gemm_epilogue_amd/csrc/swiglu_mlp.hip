@@ -353,8 +353,9 @@ int run_skinny(const void* X, int64_t ldx, const void* W, int64_t M, int64_t N, 
   return launch_status();
 }
 
+// residual: nullptr, or x itself for the residual block (Dout == D)
 int fwd_skinny(const void* x, const void* W1, const void* Wd, void* preact, void* y, void* h, float* partial,
-               int64_t M, int64_t D, int64_t I, int64_t Dout, hipStream_t st) {
+               int64_t M, int64_t D, int64_t I, int64_t Dout, hipStream_t st, const void* residual = nullptr) {
   int S;
   SW_TRY(run_skinny(x, D, W1, M, 2 * I, D, partial, st, &S));
   const int64_t t1 = M * (I / 8);
@@ -364,7 +365,7 @@ int fwd_skinny(const void* x, const void* W1, const void* Wd, void* preact, void
   SW_TRY(run_skinny(h, I, Wd, M, Dout, I, partial, st, &S));
   const int64_t t2 = M * (Dout / 8);
   hipLaunchKernelGGL(skinny_store_reduce_kernel, dim3((unsigned)((t2 + 255) / 256)), dim3(256), 0, st, partial, S,
-                     (int)M, Dout, (uint16_t*)y);
+                     (int)M, Dout, (uint16_t*)y, (const uint16_t*)residual);
   return launch_status();
 }
 
@@ -390,6 +391,20 @@ int step_dgrad_fused(const void* dy, const void* Wd, const void* preact, void* g
                      int64_t Dout, hipStream_t st) {
   EpiSwigluBwd::Params ep{cu16(preact), u16(gp), u16(h), I};
   return run_gemm_auto<true, true, EpiSwigluBwd>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, 0, ep, st);
+}
+
+// residual-add epilogues (Lesson 24, section 24): y = x + h.W_down and, in
+// the backward of the residual block, dx = grad_preact.W1^T + dy
+int step_down_residual(const void* h, const void* Wd, const void* x, void* y, int64_t M, int64_t I, int64_t D,
+                       hipStream_t st) {
+  EpiStoreResidual::Params ep{u16(y), D, cu16(x), D};
+  return run_gemm_auto<true, false, EpiStoreResidual>(cu16(h), I, cu16(Wd), D, M, D, I, 0, ep, st);
+}
+
+int step_dx_residual(const void* gp, const void* W1, const void* dy, void* dx, int64_t M, int64_t D, int64_t I,
+                     hipStream_t st) {
+  EpiStoreResidual::Params ep{u16(dx), D, cu16(dy), D};
+  return run_gemm_auto<true, true, EpiStoreResidual>(cu16(gp), 2 * I, cu16(W1), 2 * I, M, D, 2 * I, 0, ep, st);
 }
 
 int step_dgrad_fused_gp(const void* dy, const void* Wd, const void* preact, void* gp, int64_t M, int64_t I,
@@ -461,7 +476,7 @@ const char* swiglu_status_string(int status) {
   }
 }
 
-int swiglu_abi_version(void) { return (1 << 16) | 1; }
+int swiglu_abi_version(void) { return (1 << 16) | 2; }
 
 size_t swiglu_mlp_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
   if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
@@ -543,6 +558,84 @@ int swiglu_mlp_bwd_unfused(const void* x, const void* W1, const void* W_down, co
                            void* dx, void* dW1, void* dW_down, void* ws, size_t ws_bytes, int64_t M, int64_t D,
                            int64_t I, int64_t Dout, void* stream) {
   return bwd_common(false, x, W1, W_down, preact, dy, dx, dW1, dW_down, ws, ws_bytes, M, D, I, Dout, stream);
+}
+
+// --- residual block Y = X + MLP(X) (Lesson 24, section 24) ------------------
+
+int swiglu_mlp_fwd_residual(const void* x, const void* W1, const void* W_down, void* preact, void* y, void* ws,
+                            size_t ws_bytes, int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(check_dims(M, D, I, Dout));
+  if (Dout != D) return SWIGLU_ERR_SHAPE;
+  if (missing(x, M * D) || !W1 || !W_down || missing(preact, M * I) || missing(y, M * Dout))
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned16(preact) || !aligned16(y) ||
+      (ws && !aligned16(ws)))
+    return SWIGLU_ERR_ALIGN;
+  const size_t need = swiglu_mlp_fwd_workspace(M, D, I, Dout);
+  if (need > 0 && (!ws || ws_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2)};
+  const Range outs[] = {rng(preact, M * 2 * I * 2), rng(y, M * Dout * 2), rng(ws, (int64_t)need)};
+  SW_TRY(check_alias(ins, 3, outs, 3));
+  hipStream_t st = as_stream(stream);
+  if (fwd_is_skinny(M, I, Dout))
+    return fwd_skinny(x, W1, W_down, preact, y, ws, (float*)((char*)ws + align256((size_t)(M * I * 2))), M, D, I,
+                      Dout, st, x);
+  SW_TRY(step_gemm1(x, W1, preact, ws, M, D, I, st));
+  return step_down_residual(ws, W_down, x, y, M, I, D, st);
+}
+
+int swiglu_mlp_bwd_residual(const void* x, const void* W1, const void* W_down, const void* preact, const void* dy,
+                            void* dx, void* dW1, void* dW_down, void* ws, size_t ws_bytes, int64_t M, int64_t D,
+                            int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(check_dims(M, D, I, Dout));
+  if (Dout != D) return SWIGLU_ERR_SHAPE;
+  if (missing(x, M * D) || !W1 || !W_down || missing(preact, M * I) || missing(dy, M * Dout) ||
+      missing(dx, M * D) || !dW1 || !dW_down)
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned16(preact) || !aligned16(dy) ||
+      !aligned16(dx) || !aligned16(dW1) || !aligned16(dW_down) || (ws && !aligned16(ws)))
+    return SWIGLU_ERR_ALIGN;
+  const size_t need = swiglu_mlp_bwd_workspace(M, D, I, Dout);
+  if (need > 0 && (!ws || ws_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2),
+                       rng(preact, M * 2 * I * 2), rng(dy, M * Dout * 2)};
+  const Range outs[] = {rng(dx, M * D * 2), rng(dW1, D * 2 * I * 2), rng(dW_down, I * Dout * 2),
+                        rng(ws, (int64_t)need)};
+  SW_TRY(check_alias(ins, 5, outs, 4));
+  hipStream_t st = as_stream(stream);
+  char* w = (char*)ws;
+  void* gp = w;
+  void* h = w + align256((size_t)(M * 2 * I * 2));
+  SW_TRY(step_dgrad_fused(dy, W_down, preact, gp, h, M, I, Dout, st));
+  SW_TRY(step_dw_down(h, dy, dW_down, M, I, Dout, st));
+  SW_TRY(step_dx_residual(gp, W1, dy, dx, M, D, I, st));
+  return step_dw1(x, gp, dW1, M, D, I, st);
+}
+
+int swiglu_fwd_down_residual(const void* h, const void* W_down, const void* x, void* y, int64_t M, int64_t I,
+                             int64_t D, void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(I));
+  SW_TRY(check_inner(D));
+  if (missing(h, M * I) || !W_down || missing(x, M * D) || missing(y, M * D)) return SWIGLU_ERR_NULL;
+  if (!aligned16(h) || !aligned16(W_down) || !aligned16(x) || !aligned16(y)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(h, M * I * 2), rng(W_down, I * D * 2), rng(x, M * D * 2)};
+  const Range outs[] = {rng(y, M * D * 2)};
+  SW_TRY(check_alias(ins, 3, outs, 1));
+  return step_down_residual(h, W_down, x, y, M, I, D, as_stream(stream));
+}
+
+int swiglu_bwd_dx_residual(const void* grad_preact, const void* W1, const void* dy, void* dx, int64_t M, int64_t D,
+                           int64_t I, void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(D));
+  SW_TRY(check_inner(I));
+  if (missing(grad_preact, M * I) || !W1 || missing(dy, M * D) || missing(dx, M * D)) return SWIGLU_ERR_NULL;
+  if (!aligned16(grad_preact) || !aligned16(W1) || !aligned16(dy) || !aligned16(dx)) return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(grad_preact, M * 2 * I * 2), rng(W1, D * 2 * I * 2), rng(dy, M * D * 2)};
+  const Range outs[] = {rng(dx, M * D * 2)};
+  SW_TRY(check_alias(ins, 3, outs, 1));
+  return step_dx_residual(grad_preact, W1, dy, dx, M, D, I, as_stream(stream));
 }
 
 // --- save-h fallback (the drop-h report's normal MLPBlock) ------------------

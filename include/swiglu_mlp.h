@@ -67,7 +67,7 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* swiglu_status_string(int status);
 
-/* ABI version of this header, (major << 16) | minor: 1.1. */
+/* ABI version of this header, (major << 16) | minor: 1.2. */
 int swiglu_abi_version(void);
 
 /* ---------------------------------------------------------------------------
@@ -147,6 +147,30 @@ int swiglu_mlp_bwd_saved_h(const void* x, const void* W1, const void* W_down, co
                            int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Residual block Y = X + MLP(X) (Lesson 24, section 24, the residual-add
+ * epilogue).  Requires Dout == D (else SWIGLU_ERR_SHAPE).  The add happens in
+ * the epilogue of the GEMM that produces the MLP output, in fp32 before the
+ * single bf16 rounding, so the bare MLP output never reaches HBM.  Same saved
+ * set and workspaces as the drop-h calls.
+ * ------------------------------------------------------------------------- */
+
+/* As swiglu_mlp_fwd, with y = rn(x + h.W_down) [M,D].  Workspace: the
+ * swiglu_mlp_fwd_workspace query. */
+int swiglu_mlp_fwd_residual(const void* x, const void* W1, const void* W_down,
+                            void* preact, void* y,
+                            void* ws, size_t ws_bytes,
+                            int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
+
+/* As swiglu_mlp_bwd, with dx = rn(grad_preact.W1^T + dy): the identity
+ * branch's gradient joins in the dx GEMM's epilogue.  dW1 and dW_down are the
+ * plain MLP's.  Workspace: the swiglu_mlp_bwd_workspace query. */
+int swiglu_mlp_bwd_residual(const void* x, const void* W1, const void* W_down, const void* preact,
+                            const void* dy,
+                            void* dx, void* dW1, void* dW_down,
+                            void* ws, size_t ws_bytes,
+                            int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Single steps (each is one kernel launch; used by the whole-step calls
  * above, exported for timing and for step-level parity tests)
  * ------------------------------------------------------------------------- */
@@ -177,6 +201,16 @@ int swiglu_bwd_dgrad_fused(const void* dy, const void* W_down, const void* preac
  * grad_preact [M,2I]. */
 int swiglu_bwd_dgrad_fused_gp(const void* dy, const void* W_down, const void* preact,
                               void* grad_preact, int64_t M, int64_t I, int64_t Dout, void* stream);
+
+/* Down GEMM with the residual-add epilogue: y = rn(h.W_down + x).
+ * h [M,I], W_down [I,D], x [M,D] -> y [M,D]. */
+int swiglu_fwd_down_residual(const void* h, const void* W_down, const void* x, void* y,
+                             int64_t M, int64_t I, int64_t D, void* stream);
+
+/* dx GEMM with the residual-add epilogue: dx = rn(grad_preact.W1^T + dy).
+ * grad_preact [M,2I], W1 [D,2I], dy [M,D] -> dx [M,D]. */
+int swiglu_bwd_dx_residual(const void* grad_preact, const void* W1, const void* dy, void* dx,
+                           int64_t M, int64_t D, int64_t I, void* stream);
 
 /* Baseline dgrad GEMM: dout = dy . W_down^T rounded to bf16 and stored.
  * dy [M,Dout], W_down [I,Dout] -> dout [M,I]. */

@@ -157,6 +157,38 @@ def test_save_h_entry_points_reject_bad_arguments():
     assert L.swiglu_bwd_dgrad_fused_gp(a[0], a[1], a[2], a[3], M, 100, Dout, None) == UNSUP
 
 
+def test_residual_entry_points_reject_bad_arguments():
+    L = sw.lib()
+    M, D, I = 128, 256, 512
+    fwd = lambda p, Dout=D, wsb=1 << 40: L.swiglu_mlp_fwd_residual(*p[:5], p[5], wsb, M, D, I, Dout, None)
+    p = [addr(i) for i in range(6)]
+    assert fwd(p, Dout=D + 64) == SHAPE                       # the identity branch needs Dout == D
+    for k in range(5):
+        q = list(p); q[k] = None
+        assert fwd(q) == NULL, k
+    assert fwd(p, wsb=10) == WS
+    q = list(p); q[4] = addr(0)                               # y onto x
+    assert fwd(q) == ALIAS
+    q = list(p); q[4] = p[4] + 8
+    assert fwd(q) == ALIGN
+    bwd = lambda p, Dout=D, wsb=1 << 40: L.swiglu_mlp_bwd_residual(*p[:8], p[8], wsb, M, D, I, Dout, None)
+    p = [addr(i) for i in range(9)]
+    assert bwd(p, Dout=D - 64) == SHAPE
+    for k in range(8):
+        q = list(p); q[k] = None
+        assert bwd(q) == NULL, k
+    assert bwd(p, wsb=10) == WS
+    q = list(p); q[5] = addr(4)                               # dx onto dy
+    assert bwd(q) == ALIAS
+    a = [addr(i) for i in range(4)]
+    assert L.swiglu_fwd_down_residual(a[0], a[1], a[2], a[2], M, I, D, None) == ALIAS
+    assert L.swiglu_fwd_down_residual(a[0], a[1], None, a[3], M, I, D, None) == NULL
+    assert L.swiglu_fwd_down_residual(a[0], a[1], a[2], a[3], M, I, 100, None) == UNSUP
+    assert L.swiglu_bwd_dx_residual(a[0], a[1], a[2], a[2], M, D, I, None) == ALIAS
+    assert L.swiglu_bwd_dx_residual(a[0], a[1], None, a[3], M, D, I, None) == NULL
+    assert L.swiglu_bwd_dx_residual(a[0], a[1], a[2], a[3], -1, D, I, None) == SHAPE
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(4, 64, dtype=torch.bfloat16)

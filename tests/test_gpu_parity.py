@@ -11,7 +11,7 @@ import torch
 
 import bwd_gemm_epilogue_amd as sw
 import oracle
-from gpu_util import assert_close, assert_ulp, bits, to_dev, to_f64
+from gpu_util import assert_close, assert_ulp, bits, to_dev, to_f64, ulp_bf16
 from workload import WORKLOADS, bf16_bits_to_f64, make_custom, make_inputs, round_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -202,6 +202,60 @@ def test_save_h_autograd_saves_five_tensors():
         grads.append([bits(t) for t in (y.reshape(-1, Dout), x3.grad.reshape(-1, D), W1r.grad, Wdr.grad)])
     for a, b in zip(*grads):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("shape", [(200, 256, 512, 256), (300, 512, 768, 512), (96, 192, 320, 192),
+                                   (2048, 1024, 2816, 1024), (1, 256, 512, 256), (13, 384, 192, 384),
+                                   (16, 1024, 2816, 1024)])
+def test_residual_block_vs_oracle(shape):
+    """Y = X + MLP(X) with the add in the down GEMM's epilogue (the last
+    three shapes take the decode path, whose reduce kernel adds x), and
+    dX = dy + grad_preact.W1^T with dy added in the dx GEMM's epilogue.
+    Checked against the oracle's residual block, the bare MLP part (y - x,
+    dx - dy) against the oracle's MLP, and the gradients that the identity
+    branch does not touch bitwise against the plain MLP's."""
+    M, D, I, Dout = shape
+    _case("residual block", shape)
+    _, (x, W1, Wd, dy), (xf, W1f, Wdf, dyf) = _inputs(M, D, I, Dout, seed=31)
+    pre, y = sw.swiglu_mlp_fwd_residual(x, W1, Wd)
+    pre0, y0 = sw.swiglu_mlp_fwd(x, W1, Wd)
+    dx, dW1, dWd = sw.swiglu_mlp_bwd_residual(x, W1, Wd, pre, dy)
+    dx0, dW10, dWd0 = sw.swiglu_mlp_bwd(x, W1, Wd, pre0, dy)
+    torch.cuda.synchronize()
+    for a, b in ((pre, pre0), (dW1, dW10), (dWd, dWd0)):
+        assert np.array_equal(bits(a), bits(b))
+    ref = oracle.backward_residual(xf, W1f, Wdf, dyf)
+    plain = oracle.backward(xf, W1f, Wdf, dyf)
+    assert_close("y", to_f64(y), ref["y"])
+    assert_close("dx", to_f64(dx), ref["dx"])
+    assert_close("y - x", to_f64(y) - xf, plain["y"])
+    assert_close("dx - dy", to_f64(dx) - dyf, plain["dx"])
+    # one rounding of (acc + x): within one bf16 ulp of y on each side of
+    # the separately rounded MLP output plus x
+    yr, y0f = to_f64(y), to_f64(y0)
+    assert np.all(np.abs(yr - (y0f + xf)) <= ulp_bf16(yr) + ulp_bf16(y0f))
+    dxr, dx0f = to_f64(dx), to_f64(dx0)
+    assert np.all(np.abs(dxr - (dx0f + dyf)) <= ulp_bf16(dxr) + ulp_bf16(dx0f))
+
+
+def test_residual_step_kernels_and_autograd():
+    B, S, D, I = 2, 96, 256, 512
+    M = B * S
+    _case("residual steps + autograd")
+    _, (x, W1, Wd, dy), _ = _inputs(M, D, I, D, seed=37)
+    pre, y = sw.swiglu_mlp_fwd_residual(x, W1, Wd)
+    _, h = sw.swiglu_fwd_gemm1(x, W1)
+    assert np.array_equal(bits(sw.swiglu_fwd_down_residual(h, Wd, x)), bits(y))
+    gp, _ = sw.swiglu_bwd_dgrad_fused(dy, Wd, pre)
+    dx, _, _ = sw.swiglu_mlp_bwd_residual(x, W1, Wd, pre, dy)
+    assert np.array_equal(bits(sw.swiglu_bwd_dx_residual(gp, W1, dy)), bits(dx))
+    x3 = x.view(B, S, D).clone().requires_grad_(True)
+    W1r, Wdr = W1.clone().requires_grad_(True), Wd.clone().requires_grad_(True)
+    out = sw.swiglu_mlp_residual(x3, W1r, Wdr)
+    assert len(out.grad_fn.saved_tensors) == 4
+    out.backward(dy.view(B, S, D))
+    assert np.array_equal(bits(out.reshape(-1, D)), bits(y))
+    assert np.array_equal(bits(x3.grad.reshape(-1, D)), bits(dx))
 
 
 def test_empty_batch():
