@@ -179,6 +179,44 @@ def backward_residual(x, W1, Wd, dy):
     return g
 
 
+def stack_forward(x, layers):
+    """A stack of MLP blocks applied one after another (the drop-h report's
+    4-layer stack benchmark): x_0 = x, x_{l+1} = MLP_l(x_l), each block with
+    its own (W1, W_down) and Dout = D.  Returns (preacts, hs, ys), one entry
+    per layer, with ys[-1] the stack's output."""
+    cur = np.asarray(x, dtype=np.float64)
+    preacts, hs, ys = [], [], []
+    for W1, Wd in layers:
+        p, h, y = forward(cur, W1, Wd)
+        if y.shape != cur.shape:
+            raise ValueError("a stack of blocks needs Dout == D")
+        preacts.append(p)
+        hs.append(h)
+        ys.append(y)
+        cur = y
+    return preacts, hs, ys
+
+
+def stack_backward(x, layers, dy):
+    """Backward of stack_forward by the chain rule: the last block gets dy,
+    and each block's dx is the dy of the block before it.  Returns
+    {"y": the stack's output, "dx": the gradient of x, "dW1": [...],
+    "dW_down": [...]} with one weight gradient per layer."""
+    cur = np.asarray(x, dtype=np.float64)
+    inputs = []
+    for W1, Wd in layers:
+        inputs.append(cur)
+        _, _, cur = forward(cur, W1, Wd)
+    g = np.asarray(dy, dtype=np.float64)
+    dW1s, dWds = [None] * len(layers), [None] * len(layers)
+    for l in range(len(layers) - 1, -1, -1):
+        W1, Wd = layers[l]
+        r = backward(inputs[l], W1, Wd, g)
+        dW1s[l], dWds[l] = r["dW1"], r["dW_down"]
+        g = r["dx"]
+    return {"y": cur, "dx": g, "dW1": dW1s, "dW_down": dWds}
+
+
 def sampled_forward_backward(x, W1, Wd, dy, rows, chans):
     """Exact fp64 values of the outputs at a sample of positions, for shapes
     where the full oracle is too slow.  Same definitions as ``backward``,

@@ -168,6 +168,40 @@ def test_residual_block_matches_finite_differences():
         oracle.forward_residual(x, W1, _rand((I, D + 1), rng))
 
 
+def test_stack_gradients_match_finite_differences():
+    """The stacked blocks' chain rule (the drop-h report's 4-layer stack):
+    every layer's weight gradients and the input gradient against central
+    differences of <dy, Y> through three blocks."""
+    rng = np.random.default_rng(5)
+    M, D, I, L = 3, 5, 4, 3
+    x = _rand((M, D), rng)
+    layers = [(_rand((D, 2 * I), rng, 0.8), _rand((I, D), rng, 0.6)) for _ in range(L)]
+    dy = _rand((M, D), rng)
+    g = oracle.stack_backward(x, layers, dy)
+
+    def loss():
+        return float(np.sum(oracle.stack_forward(x, layers)[2][-1] * dy))
+
+    assert np.array_equal(g["y"], oracle.stack_forward(x, layers)[2][-1])
+    eps = 1e-6
+    targets = [("x", x, g["dx"])]
+    for l in range(L):
+        targets += [(f"W1[{l}]", layers[l][0], g["dW1"][l]), (f"Wd[{l}]", layers[l][1], g["dW_down"][l])]
+    for name, arr, grad in targets:
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            orig = arr[idx]
+            arr[idx] = orig + eps
+            lp = loss()
+            arr[idx] = orig - eps
+            lm = loss()
+            arr[idx] = orig
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+    with pytest.raises(ValueError):
+        oracle.stack_forward(x, [(layers[0][0], _rand((I, D + 1), rng))])
+
+
 def test_grad_preact_matches_finite_differences():
     rng = np.random.default_rng(7)
     M, I, Dout = 4, 6, 3
