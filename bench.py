@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="target")
     ap.add_argument("--ab-pairs", type=int, default=40)
+    ap.add_argument("--stack-layers", type=int, default=4, help="blocks in the stacked workload (0: skip)")
+    ap.add_argument("--stack-iters", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -251,6 +253,59 @@ def main():
                     "separate_add_hbm_bytes_avoided": 2 * 3 * M * D * 2,
                     "separate_add_ms_at_hbm_peak": round(2 * 3 * M * D * 2 / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}
 
+    # ---- stack of blocks (the drop-h report's 4-layer stack): forward,
+    # backward and full ms through the autograd functions, after-forward and
+    # peak allocated MiB above the inputs, drop-h vs save-h in alternation.
+    # Layers 1..L-1 hold copies of layer 0's weight values (the same seeded
+    # distribution; one more target-shape weight set costs ~20 s of CPU).
+    stack = None
+    if D == Dout and args.stack_layers > 0:
+        L = args.stack_layers
+        layers = [(W1.clone().requires_grad_(True), Wd.clone().requires_grad_(True)) for _ in range(L)]
+        xs = x.clone().requires_grad_(True)
+        res = {False: [], True: []}
+        mem = {}
+        # pass 0 measures memory from an emptied allocator cache (allocations
+        # then land in fresh segments, as in a fresh process) and is not timed;
+        # the timed passes run with a warm cache
+        for it in range(1 + args.stack_iters):
+            for save_h in (False, True):
+                for W in (xs, *[w for pair in layers for w in pair]):
+                    W.grad = None
+                torch.cuda.synchronize()
+                if it == 0:
+                    torch.cuda.empty_cache()
+                base = torch.cuda.memory_allocated()
+                torch.cuda.reset_peak_memory_stats()
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record()
+                out = sw.swiglu_mlp_stack(xs, layers, save_h=save_h)
+                e[1].record()
+                torch.cuda.synchronize()
+                after = torch.cuda.memory_allocated() - base
+                out.backward(dy)
+                e[2].record()
+                torch.cuda.synchronize()
+                peak = torch.cuda.max_memory_allocated() - base
+                del out
+                if it > 0:
+                    res[save_h].append((e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])))
+                else:
+                    mem[save_h] = (after, peak)
+        stack = {"layers": L, "iters": args.stack_iters}
+        for save_h, tag in ((False, "drop_h"), (True, "save_h")):
+            f = float(np.median([a for a, _ in res[save_h]]))
+            b = float(np.median([b for _, b in res[save_h]]))
+            stack[tag] = {"fwd_ms": round(f, 4), "bwd_ms": round(b, 4), "full_ms": round(f + b, 4),
+                          "after_fwd_MiB": round(mem[save_h][0] / 2**20, 3), "peak_MiB": round(mem[save_h][1] / 2**20, 3)}
+        stack["after_fwd_saving_MiB"] = round((mem[True][0] - mem[False][0]) / 2**20, 3)
+        stack["after_fwd_saving_expected_MiB"] = round(L * M * I * 2 / 2**20, 3)
+        # the saved tensors' own bytes (the allocator's figure adds the slack
+        # of blocks it does not split)
+        stack["saved_tensor_MiB"] = {"drop_h": round(L * (M * 2 * I * 2 + M * D * 2) / 2**20, 3),
+                                     "save_h": round(L * (M * 2 * I * 2 + M * D * 2 + M * I * 2) / 2**20, 3)}
+        del layers, xs
+
     # ---- roofline of the fused dgrad kernel ----
     roofline = {"kernel": "bwd_dgrad_fused", "bound": "mfma", "achieved": round(b1_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(b1_tflops / PEAK_BF16_TFLOPS, 4),
@@ -283,6 +338,7 @@ def main():
         "ab_fused_vs_unfused": ab,
         "save_h_variant": save_h,
         "residual_block": residual,
+        "stack": stack,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_digest": source_digest(),

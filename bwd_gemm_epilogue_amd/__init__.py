@@ -29,6 +29,7 @@ __all__ = [
     "swiglu_bwd_dgrad_fused_gp", "SwiGLUMLPSaveHFunction", "swiglu_mlp_save_h",
     "swiglu_mlp_fwd_residual", "swiglu_mlp_bwd_residual", "swiglu_fwd_down_residual",
     "swiglu_bwd_dx_residual", "SwiGLUResidualMLPFunction", "swiglu_mlp_residual",
+    "swiglu_mlp_stack",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -470,3 +471,16 @@ class SwiGLUResidualMLPFunction(torch.autograd.Function):
 
 def swiglu_mlp_residual(x, W1, W_down):
     return SwiGLUResidualMLPFunction.apply(x, W1, W_down)
+
+
+def swiglu_mlp_stack(x, layers, save_h=False):
+    """A stack of MLP blocks applied in order (the drop-h report's 4-layer
+    stack): x_{l+1} = MLP_l(x_l) for layers = [(W1_l, W_down_l), ...], each
+    with Dout == D.  Every block is its own autograd node, so each keeps its
+    own saved set: {x_l, W1_l, W_down_l, preact_l}, plus h_l with save_h."""
+    fn = swiglu_mlp_save_h if save_h else swiglu_mlp
+    for W1, W_down in layers:
+        if W_down.shape[1] != x.shape[-1]:
+            raise ValueError("a stack of blocks needs Dout == D in every layer")
+        x = fn(x, W1, W_down)
+    return x

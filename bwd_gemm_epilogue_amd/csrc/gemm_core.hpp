@@ -546,7 +546,10 @@ struct EpiStore {
 // so no intermediate GEMM output reaches HBM.  R has C's shape.
 // ---------------------------------------------------------------------------
 struct EpiStoreResidual {
-  static constexpr int kPrefetchDepth = 2;
+  // every slab's residual is requested before the first slab is stored:
+  // measured 0.04 ms over both residual GEMMs of the 11136x3584x14336 block
+  // against 0.11 ms at two slabs ahead
+  static constexpr int kPrefetchDepth = 4;
   struct Params {
     uint16_t* C;
     int64_t ldc;
