@@ -8,6 +8,6 @@ See ``oracle.swiglu`` for the functions and the passages each one follows.
 """
 from .swiglu import (  # noqa: F401
     sigmoid, silu, dsilu_form1, dsilu_form2, dsilu_form3, dsilu,
-    forward, backward, forward_residual, backward_residual, stack_forward, stack_backward, swiglu_bwd_elementwise, swiglu_fwd_elementwise,
+    forward, backward, forward_residual, backward_residual, stack_forward, stack_backward, moe_forward, moe_backward, swiglu_bwd_elementwise, swiglu_fwd_elementwise,
     sampled_forward_backward, gemm_flops, algorithmic_bytes,
 )

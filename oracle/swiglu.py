@@ -217,6 +217,51 @@ def stack_backward(x, layers, dy):
     return {"y": cur, "dx": g, "dW1": dW1s, "dW_down": dWds}
 
 
+def moe_forward(x, W1s, Wds, offsets):
+    """Mixture-of-experts MLP (Lesson 24, section 41: every expert is its own
+    MLP block; section 42: the tokens of each expert form one GEMM of their
+    own size).  Routed rows arrive packed by expert: expert e owns rows
+    [offsets[e], offsets[e+1]) and applies its block (W1s[e], Wds[e]) to
+    them.  Returns (preact, h, y) over all rows."""
+    x = np.asarray(x, dtype=np.float64)
+    off = [int(v) for v in offsets]
+    E = len(W1s)
+    if len(off) != E + 1 or off[0] != 0 or off[-1] != x.shape[0] or any(b < a for a, b in zip(off, off[1:])):
+        raise ValueError("offsets must run from 0 to the row count without decreasing, one more than the experts")
+    I = np.asarray(Wds[0]).shape[0]
+    Dout = np.asarray(Wds[0]).shape[1]
+    M = x.shape[0]
+    preact, h, y = np.zeros((M, 2 * I)), np.zeros((M, I)), np.zeros((M, Dout))
+    for e in range(E):
+        a, b = off[e], off[e + 1]
+        preact[a:b], h[a:b], y[a:b] = forward(x[a:b], W1s[e], Wds[e])
+    return preact, h, y
+
+
+def moe_backward(x, W1s, Wds, offsets, dy):
+    """Backward of moe_forward: each expert's rows take its block's backward;
+    an expert with no rows has zero weight gradients.  Returns the dict of
+    ``backward`` over all rows, with dW1 [E, D, 2I] and dW_down [E, I, Dout]
+    stacked per expert."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    preact, h, y = moe_forward(x, W1s, Wds, offsets)
+    off = [int(v) for v in offsets]
+    E = len(W1s)
+    M, D = x.shape
+    I = np.asarray(Wds[0]).shape[0]
+    out = {"preact": preact, "h": h, "y": y, "dout": np.zeros((M, I)), "grad_preact": np.zeros((M, 2 * I)),
+           "dx": np.zeros((M, D)), "dW1": np.zeros((E, D, 2 * I)), "dW_down": np.zeros((E, I, dy.shape[1]))}
+    for e in range(E):
+        a, b = off[e], off[e + 1]
+        r = backward(x[a:b], W1s[e], Wds[e], dy[a:b])
+        for k in ("dout", "grad_preact", "dx"):
+            out[k][a:b] = r[k]
+        out["dW1"][e] = r["dW1"]
+        out["dW_down"][e] = r["dW_down"]
+    return out
+
+
 def sampled_forward_backward(x, W1, Wd, dy, rows, chans):
     """Exact fp64 values of the outputs at a sample of positions, for shapes
     where the full oracle is too slow.  Same definitions as ``backward``,

@@ -202,6 +202,56 @@ def test_stack_gradients_match_finite_differences():
         oracle.stack_forward(x, [(layers[0][0], _rand((I, D + 1), rng))])
 
 
+def test_moe_gradients_match_finite_differences():
+    """The mixture-of-experts block (Lesson 24, sections 41-42): every
+    expert's weight gradients and the routed rows' dx against central
+    differences of <dy, Y>, with an expert that receives no rows (zero
+    gradients) and one that receives a single row."""
+    rng = np.random.default_rng(11)
+    D, I, Dout = 4, 3, 5
+    counts = [2, 0, 3, 1]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    M, E = int(off[-1]), len(counts)
+    x, dy = _rand((M, D), rng), _rand((M, Dout), rng)
+    W1s = [_rand((D, 2 * I), rng, 0.8) for _ in range(E)]
+    Wds = [_rand((I, Dout), rng, 0.6) for _ in range(E)]
+    g = oracle.moe_backward(x, W1s, Wds, off, dy)
+    assert np.all(g["dW1"][1] == 0) and np.all(g["dW_down"][1] == 0)
+
+    def loss():
+        return float(np.sum(oracle.moe_forward(x, W1s, Wds, off)[2] * dy))
+
+    eps = 1e-6
+    targets = [("x", x, g["dx"])]
+    for e in range(E):
+        targets += [(f"W1[{e}]", W1s[e], g["dW1"][e]), (f"Wd[{e}]", Wds[e], g["dW_down"][e])]
+    for name, arr, grad in targets:
+        for _ in range(8):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            orig = arr[idx]
+            arr[idx] = orig + eps
+            lp = loss()
+            arr[idx] = orig - eps
+            lm = loss()
+            arr[idx] = orig
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+    for bad in ([0, 2, 2, 5, 5], [0, 3, 2, 5, 6], [1, 2, 2, 5, 6]):
+        with pytest.raises(ValueError):
+            oracle.moe_forward(x, W1s, Wds, bad)
+
+
+def test_moe_with_one_expert_is_the_dense_block():
+    rng = np.random.default_rng(13)
+    M, D, I, Dout = 5, 4, 3, 2
+    x, W1, Wd, dy = _rand((M, D), rng), _rand((D, 2 * I), rng), _rand((I, Dout), rng), _rand((M, Dout), rng)
+    g = oracle.moe_backward(x, [W1], [Wd], [0, M], dy)
+    r = oracle.backward(x, W1, Wd, dy)
+    for k in ("y", "dx", "grad_preact"):
+        assert np.array_equal(g[k], r[k])
+    assert np.array_equal(g["dW1"][0], r["dW1"]) and np.array_equal(g["dW_down"][0], r["dW_down"])
+
+
 def test_grad_preact_matches_finite_differences():
     rng = np.random.default_rng(7)
     M, I, Dout = 4, 6, 3

@@ -37,3 +37,24 @@ def test_llama_gate_half_is_scaled_by_8():
 def test_workload_shapes():
     for name, w in WORKLOADS.items():
         assert w.D % 64 == 0 and w.I % 64 == 0 and w.Dout % 64 == 0, name
+
+
+def test_moe_routing_counts_and_offsets():
+    from workload import MOE_WORKLOADS, expert_counts, group_offsets, make_moe_inputs
+    w = MOE_WORKLOADS["moe"]
+    c = expert_counts(w.tokens, w.top_k, w.experts, w.skew)
+    assert c.shape == (w.experts,) and c.sum() == w.M and np.all(c >= 0)
+    assert np.array_equal(c, expert_counts(w.tokens, w.top_k, w.experts, w.skew))
+    assert c.max() > 2 * c.min()                      # uneven: the grouped GEMM's case
+    # each token picks distinct experts: no expert can hold more rows than tokens
+    assert c.max() <= w.tokens
+    off = group_offsets(c)
+    assert off.dtype == np.int32 and off[0] == 0 and off[-1] == w.M and np.all(np.diff(off) == c)
+    t = MOE_WORKLOADS["moe_tiny"]
+    x, W1, Wd, dy, o = make_moe_inputs(t)
+    assert x.shape == (t.M, t.D) and dy.shape == (t.M, t.Dout)
+    assert W1.shape == (t.experts, t.D, 2 * t.I) and Wd.shape == (t.experts, t.I, t.Dout)
+    assert o[-1] == t.M and len({W1[e].tobytes() for e in range(t.experts)}) == t.experts
+    _, W1s, _, _, _ = make_moe_inputs(t, weight_sets=2)
+    assert np.array_equal(W1s[0], W1s[2]) and not np.array_equal(W1s[0], W1s[1])
+    assert np.array_equal(W1s[1], W1[1])

@@ -22,6 +22,9 @@ import numpy as np
 BASE_SEED = 1234
 # one seed offset per tensor, so every tensor is reproducible on its own
 SEED_X, SEED_W1, SEED_WD, SEED_DY = 0, 1, 2, 3
+# expert routing of the MoE workloads; expert e's weights use seed offsets
+# SEED_W1 + 16 * (e + 1) and SEED_WD + 16 * (e + 1)
+SEED_ROUTE = 4
 
 
 @dataclass(frozen=True)
@@ -133,3 +136,97 @@ def make_custom(M: int, D: int, I: int, Dout: int, seed: int = BASE_SEED,
     w = Workload("custom", M, D, I, Dout, x_std, _fan_in(D), _fan_in(I), dy_std,
                  gate_scale=gate_scale)
     return make_inputs(w, seed)
+
+
+# ---------------------------------------------------------------------------
+# Mixture-of-experts workloads ("Lesson 24", sections 41-43): every expert is
+# its own SwiGLU MLP block, tokens are routed to top_k experts each, and the
+# routed rows arrive sorted and packed by expert, so that expert e owns rows
+# [offsets[e], offsets[e+1]).  Routing itself is not modelled: the expert of
+# each routed row is drawn from a skewed (Zipf-like) popularity, which gives
+# the uneven per-expert token counts the grouped GEMM is for.  The routed
+# rows of x and dy are independent draws (the GEMMs do not care whether two
+# rows are copies of one token).
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class MoEWorkload:
+    name: str
+    tokens: int       # tokens before routing
+    top_k: int        # experts per token
+    experts: int
+    D: int
+    I: int            # each expert's intermediate size
+    Dout: int
+    x_std: float
+    w1_std: float
+    wd_std: float
+    dy_std: float
+    skew: float       # popularity of the r-th most popular expert ~ 1 / r**skew
+    note: str = field(default="", compare=False)
+
+    @property
+    def M(self) -> int:
+        """Routed rows: tokens * top_k."""
+        return self.tokens * self.top_k
+
+
+MOE_WORKLOADS = {
+    "moe_tiny": MoEWorkload("moe_tiny", 160, 2, 8, 256, 256, 256,
+                            1.0, _fan_in(256), _fan_in(256), 1.0, skew=1.0,
+                            note="correctness case; full oracle in seconds"),
+    "moe": MoEWorkload("moe", 8192, 2, 16, 3584, 2048, 3584,
+                       1.0, _fan_in(3584), _fan_in(2048), 1.0, skew=0.8,
+                       note="16 experts of width 2048 on the target model dimension, top-2 routing"),
+}
+
+
+def expert_counts(tokens: int, top_k: int, experts: int, skew: float, seed: int = BASE_SEED) -> np.ndarray:
+    """Routed rows per expert: each token picks top_k distinct experts, drawn
+    without replacement from a Zipf-like popularity over a seeded random
+    order of the experts (Gumbel top-k).  Returns int64 [experts] summing to
+    tokens * top_k."""
+    if not 1 <= top_k <= experts:
+        raise ValueError("need 1 <= top_k <= experts")
+    rng = np.random.Generator(np.random.PCG64(seed + SEED_ROUTE))
+    p = 1.0 / np.arange(1, experts + 1, dtype=np.float64) ** skew
+    p = p[rng.permutation(experts)]
+    keys = np.log(p)[None, :] + rng.gumbel(size=(tokens, experts))
+    chosen = np.argpartition(-keys, top_k - 1, axis=1)[:, :top_k]
+    return np.bincount(chosen.ravel(), minlength=experts).astype(np.int64)
+
+
+def group_offsets(counts) -> np.ndarray:
+    """int32 [E + 1] row offsets of the expert-packed rows: 0, c0, c0 + c1, ..."""
+    counts = np.asarray(counts, dtype=np.int64)
+    if np.any(counts < 0):
+        raise ValueError("negative count")
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def make_moe_inputs(w: MoEWorkload, seed: int = BASE_SEED, weight_sets: int | None = None, counts=None):
+    """bf16 bit patterns for x [M, D], W1 [E, D, 2I], W_down [E, I, Dout],
+    dy [M, Dout], and the int32 offsets [E + 1], with M = tokens * top_k.
+
+    ``weight_sets`` < E draws that many distinct expert weight sets and gives
+    expert e the set e % weight_sets (a timing shortcut: the values keep the
+    same distribution); by default every expert has its own.  ``counts``
+    overrides the routed rows per expert."""
+    if counts is None:
+        counts = expert_counts(w.tokens, w.top_k, w.experts, w.skew, seed)
+    counts = np.asarray(counts, dtype=np.int64)
+    if counts.shape != (w.experts,):
+        raise ValueError("one count per expert")
+    M = int(counts.sum())
+    nsets = w.experts if weight_sets is None else max(1, min(int(weight_sets), w.experts))
+    x = normal_bf16((M, w.D), w.x_std, seed + SEED_X)
+    dy = normal_bf16((M, w.Dout), w.dy_std, seed + SEED_DY)
+    W1 = np.empty((w.experts, w.D, 2 * w.I), dtype=np.uint16)
+    Wd = np.empty((w.experts, w.I, w.Dout), dtype=np.uint16)
+    for e in range(nsets):
+        W1[e] = normal_bf16((w.D, 2 * w.I), w.w1_std, seed + SEED_W1 + 16 * (e + 1))
+        Wd[e] = normal_bf16((w.I, w.Dout), w.wd_std, seed + SEED_WD + 16 * (e + 1))
+    for e in range(nsets, w.experts):
+        W1[e] = W1[e % nsets]
+        Wd[e] = Wd[e % nsets]
+    return x, W1, Wd, dy, group_offsets(counts)
