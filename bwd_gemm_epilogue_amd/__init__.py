@@ -30,6 +30,8 @@ __all__ = [
     "swiglu_mlp_fwd_residual", "swiglu_mlp_bwd_residual", "swiglu_fwd_down_residual",
     "swiglu_bwd_dx_residual", "SwiGLUResidualMLPFunction", "swiglu_mlp_residual",
     "swiglu_mlp_stack",
+    "swiglu_moe_fwd_workspace", "swiglu_moe_bwd_workspace", "swiglu_moe_fwd", "swiglu_moe_bwd",
+    "swiglu_moe_bwd_dgrad_fused", "SwiGLUMoEFunction", "swiglu_moe",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +68,11 @@ _SIGNATURES = {
     "swiglu_mlp_bwd_residual": (ctypes.c_int, [_P] * 8 + [_P, _SZ] + [_I64] * 4 + [_P]),
     "swiglu_fwd_down_residual": (ctypes.c_int, [_P] * 4 + [_I64] * 3 + [_P]),
     "swiglu_bwd_dx_residual": (ctypes.c_int, [_P] * 4 + [_I64] * 3 + [_P]),
+    "swiglu_moe_fwd_workspace": (_SZ, [_I64] * 5),
+    "swiglu_moe_bwd_workspace": (_SZ, [_I64] * 5),
+    "swiglu_moe_fwd": (ctypes.c_int, [_P] * 6 + [_P, _SZ] + [_I64] * 5 + [_P]),
+    "swiglu_moe_bwd": (ctypes.c_int, [_P] * 9 + [_P, _SZ] + [_I64] * 5 + [_P]),
+    "swiglu_moe_bwd_dgrad_fused": (ctypes.c_int, [_P] * 6 + [_I64] * 4 + [_P]),
 }
 
 
@@ -484,3 +491,98 @@ def swiglu_mlp_stack(x, layers, save_h=False):
             raise ValueError("a stack of blocks needs Dout == D in every layer")
         x = fn(x, W1, W_down)
     return x
+
+
+# --------------------------------------------------------------------------
+# mixture-of-experts blocks (grouped GEMMs over expert-packed rows)
+# --------------------------------------------------------------------------
+
+def _offsets(off, E: int) -> int:
+    if not isinstance(off, torch.Tensor) or not off.is_cuda or off.dtype != torch.int32 or not off.is_contiguous():
+        raise ValueError("group_offsets must be a contiguous int32 tensor on the GPU")
+    if tuple(off.shape) != (E + 1,):
+        raise ValueError(f"group_offsets has shape {tuple(off.shape)}, expected ({E + 1},)")
+    return off.data_ptr()
+
+
+def _dims_moe(x, W1, W_down):
+    M, D = x.shape
+    E, D2, I2 = W1.shape
+    E2, I, Dout = W_down.shape
+    if D2 != D or I2 != 2 * I or E2 != E:
+        raise ValueError(f"inconsistent shapes x{tuple(x.shape)} W1{tuple(W1.shape)} W_down{tuple(W_down.shape)}")
+    return M, D, I, Dout, E
+
+
+def swiglu_moe_fwd_workspace(M, D, I, Dout, E) -> int:
+    return lib().swiglu_moe_fwd_workspace(M, D, I, Dout, E)
+
+
+def swiglu_moe_bwd_workspace(M, D, I, Dout, E) -> int:
+    return lib().swiglu_moe_bwd_workspace(M, D, I, Dout, E)
+
+
+def swiglu_moe_fwd(x, W1, W_down, group_offsets, preact=None, y=None, ws=None, stream=None):
+    """Expert MLPs over expert-packed rows: x [M,D], W1 [E,D,2I], W_down
+    [E,I,Dout], group_offsets int32 [E+1] on the GPU.  Returns (preact, y)."""
+    M, D, I, Dout, E = _dims_moe(x, W1, W_down)
+    preact = _empty((M, 2 * I), x) if preact is None else preact
+    y = _empty((M, Dout), x) if y is None else y
+    ws = _ws(swiglu_moe_fwd_workspace(M, D, I, Dout, E), x, ws)
+    _check("swiglu_moe_fwd", lib().swiglu_moe_fwd(
+        _dev(x, "x"), _dev(W1, "W1"), _dev(W_down, "W_down"), _offsets(group_offsets, E),
+        _dev(preact, "preact", (M, 2 * I)), _dev(y, "y", (M, Dout)),
+        ws.data_ptr(), ws.numel() * ws.element_size(), M, D, I, Dout, E, _stream(x, stream)))
+    return preact, y
+
+
+def swiglu_moe_bwd(x, W1, W_down, group_offsets, preact, dy, dx=None, dW1=None, dW_down=None, ws=None,
+                   stream=None):
+    """Backward of swiglu_moe_fwd: (dx [M,D], dW1 [E,D,2I], dW_down [E,I,Dout])."""
+    M, D, I, Dout, E = _dims_moe(x, W1, W_down)
+    dx = _empty((M, D), x) if dx is None else dx
+    dW1 = _empty((E, D, 2 * I), x) if dW1 is None else dW1
+    dW_down = _empty((E, I, Dout), x) if dW_down is None else dW_down
+    ws = _ws(swiglu_moe_bwd_workspace(M, D, I, Dout, E), x, ws)
+    _check("swiglu_moe_bwd", lib().swiglu_moe_bwd(
+        _dev(x, "x"), _dev(W1, "W1"), _dev(W_down, "W_down"), _offsets(group_offsets, E),
+        _dev(preact, "preact", (M, 2 * I)), _dev(dy, "dy", (M, Dout)), _dev(dx, "dx", (M, D)),
+        _dev(dW1, "dW1", (E, D, 2 * I)), _dev(dW_down, "dW_down", (E, I, Dout)),
+        ws.data_ptr(), ws.numel() * ws.element_size(), M, D, I, Dout, E, _stream(x, stream)))
+    return dx, dW1, dW_down
+
+
+def swiglu_moe_bwd_dgrad_fused(dy, W_down, group_offsets, preact, grad_preact=None, h=None, stream=None):
+    """The grouped fused dgrad step alone: (grad_preact [M,2I], h [M,I])."""
+    M, Dout = dy.shape
+    E, I, _ = W_down.shape
+    grad_preact = _empty((M, 2 * I), dy) if grad_preact is None else grad_preact
+    h = _empty((M, I), dy) if h is None else h
+    _check("swiglu_moe_bwd_dgrad_fused", lib().swiglu_moe_bwd_dgrad_fused(
+        _dev(dy, "dy"), _dev(W_down, "W_down", (E, I, Dout)), _offsets(group_offsets, E),
+        _dev(preact, "preact", (M, 2 * I)), _dev(grad_preact, "grad_preact", (M, 2 * I)), _dev(h, "h", (M, I)),
+        M, I, Dout, E, _stream(dy, stream)))
+    return grad_preact, h
+
+
+class SwiGLUMoEFunction(torch.autograd.Function):
+    """Expert SwiGLU MLPs over expert-packed rows (Lesson 24, sections
+    41-42).  Saves {x, W1, W_down, group_offsets, preact}; h is recomputed in
+    the grouped fused dgrad's epilogue."""
+
+    @staticmethod
+    def forward(ctx, x, W1, W_down, group_offsets):
+        preact, y = swiglu_moe_fwd(x.contiguous(), W1.contiguous(), W_down.contiguous(), group_offsets)
+        ctx.save_for_backward(x, W1, W_down, group_offsets, preact)
+        return y
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        x, W1, W_down, off, preact = ctx.saved_tensors
+        dx, dW1, dW_down = swiglu_moe_bwd(x.contiguous(), W1.contiguous(), W_down.contiguous(), off, preact,
+                                          grad_y.contiguous())
+        return dx, dW1, dW_down, None
+
+
+def swiglu_moe(x, W1, W_down, group_offsets):
+    return SwiGLUMoEFunction.apply(x, W1, W_down, group_offsets)

@@ -77,7 +77,21 @@ struct GemmArgs {
   // pair_off > 0: tile tn's B columns are [tn*BN/2, tn*BN/2 + BN/2) followed by
   // [pair_off + tn*BN/2, ...): the left and gate halves of W1 side by side.
   int pair_off;
+  // Grouped GEMMs ("Lesson 24", sections 42-43: one launch for the experts'
+  // GEMMs of different sizes).  group_off [groups + 1] holds token offsets
+  // in device memory: group e owns token rows [group_off[e], group_off[e+1]).
+  // Grouped over M, the tokens are the rows of A and C and each group has its
+  // own B, group_stride_b elements apart; tiles_m is then an upper bound on
+  // the tile rows of all groups together.  Grouped over K, the tokens are
+  // the k-rows of both (MN-major) operands and each group writes its own C,
+  // group_stride_c elements apart; tiles_m x tiles_n is one group's output.
+  const int* group_off;
+  int groups;
+  int64_t group_stride_b, group_stride_c;
 };
+
+// How the kernel maps work to tiles.
+enum GroupMode { kDense = 0, kGroupM = 1, kGroupK = 2 };
 
 // ---------------------------------------------------------------------------
 // LDS layouts
@@ -292,11 +306,12 @@ __device__ __forceinline__ void step(const SWG_LDS char* As, const SWG_LDS char*
 // the 8 XCDs, so each XCD is first given a contiguous run of tile ids (its own
 // L2 then sees neighbouring tiles), and tile ids are walked in groups of
 // GROUP_M tile rows so that concurrently running tiles share A and B panels.
-__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
+__device__ __forceinline__ int xcd_linear(int pid, int total) {
   const int per = total / 8, rem = total % 8;
   const int xcd = pid % 8, local = pid / 8;
-  const int id = xcd * per + (xcd < rem ? xcd : rem) + local;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+__device__ __forceinline__ void tile_order(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int GROUP_M = 8;
   const int group = id / (GROUP_M * tiles_n);
   const int first_m = group * GROUP_M;
@@ -304,6 +319,56 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
   const int in_group = id - group * GROUP_M * tiles_n;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+}
+__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  tile_order(xcd_linear(pid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+}
+
+// Token range [lo, hi) of group e, clamped into [0, M] and made non-empty
+// only when increasing: offsets that are not a valid partition give
+// unspecified results but never an access outside the token range.
+__device__ __forceinline__ void group_range(const int* off, int e, int M, int& lo, int& hi) {
+  int a = off[e], b = off[e + 1];
+  a = a < 0 ? 0 : (a > M ? M : a);
+  b = b < a ? a : (b > M ? M : b);
+  lo = a;
+  hi = b;
+}
+
+// Grouped over M: tile row r of all groups together (group e contributes
+// ceil(size_e / BM) tile rows, in group order) -> its group's first token row
+// r0 and end row m_end.  Each wave scans 64 groups at a time: an inclusive
+// prefix sum of the tile-row counts across the lanes, then a ballot for the
+// lane whose range holds r.  False when r is past the last tile row.
+template <int BM>
+__device__ __forceinline__ bool find_group_row(const int* off, int groups, int M, int r, int& grp, int& r0,
+                                               int& m_end) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int c0 = 0; c0 < groups; c0 += 64) {
+    const int e = c0 + lane;
+    int lo = 0, hi = 0;
+    if (e < groups) group_range(off, e, M, lo, hi);
+    const int cnt = (hi - lo + BM - 1) / BM;
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += t;
+    }
+    const int excl = incl - cnt;
+    const unsigned long long hit = __ballot(r >= base + excl && r < base + incl);
+    if (hit != 0ull) {
+      const int l = __ffsll((long long)hit) - 1;
+      const int lo_l = __shfl(lo, l, 64), hi_l = __shfl(hi, l, 64), ex_l = __shfl(excl, l, 64);
+      grp = __builtin_amdgcn_readfirstlane(c0 + l);
+      r0 = __builtin_amdgcn_readfirstlane(lo_l + (r - base - ex_l) * BM);
+      m_end = __builtin_amdgcn_readfirstlane(hi_l);
+      return true;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return false;
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
@@ -318,11 +383,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <class T>
 struct SlabCtx {
   const SWG_LDS float* slab;  // [SLAB_ROWS][SLAB_LD] fp32
-  int tm, tn, s;              // tile coordinates and slab index
-  int M, N;
-  // global row of slab row sr (rows past M are not stored)
+  int r0, tn, s;              // the tile's first row, its column tile, the slab index
+  int M, N;                   // rows at or past M and columns at or past N are not stored
+  int64_t goff;               // element offset of this group's C (grouped over K), else 0
+  // global row of slab row sr
   __device__ __forceinline__ int row(int sr) const {
-    return tm * T::BM + (sr >> 5) * T::WTM + s * 32 + (sr & 31);
+    return r0 + (sr >> 5) * T::WTM + s * 32 + (sr & 31);
   }
   __device__ __forceinline__ f32x8 read8(int sr, int c) const {
     const SWG_LDS f32x4* p = (const SWG_LDS f32x4*)(slab + sr * T::SLAB_LD + c);
@@ -331,15 +397,49 @@ struct SlabCtx {
   }
 };
 
-template <class T, bool A_K, bool B_K, class Epi>
+template <class T, bool A_K, bool B_K, class Epi, int GRP = kDense>
 __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) gemm_kernel(const GemmArgs g, const typename Epi::Params ep) {
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
-  int tm, tn;
-  tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  // tile coordinates; r0 / m_end: the tile's first row and the row bound;
+  // Ag, Bg, Kg: this tile's operands and reduction length
+  int tm, tn, r0, m_end, Kg = g.K;
+  const uint16_t* Ag = g.A;
+  const uint16_t* Bg = g.B;
+  int64_t goff = 0;
+  if constexpr (GRP == kDense) {
+    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    r0 = tm * T::BM;
+    m_end = g.M;
+  } else if constexpr (GRP == kGroupM) {
+    static_assert(A_K, "grouped over M: A is the K-major token operand");
+    int r, grp;
+    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, r, tn);
+    // past the last tile row of the last group: the whole workgroup leaves
+    // (the condition is uniform across it, before any barrier)
+    if (!find_group_row<T::BM>(g.group_off, g.groups, g.M, r, grp, r0, m_end)) return;
+    tm = 0;  // K-major A is addressed from r0
+    Bg += (int64_t)grp * g.group_stride_b;
+  } else {
+    static_assert(!A_K && !B_K, "grouped over K: both operands are MN-major token operands");
+    const int per = g.tiles_m * g.tiles_n;
+    const int id = xcd_linear(blockIdx.x, per * g.groups);
+    const int grp = id / per;
+    tile_order(id - grp * per, g.tiles_m, g.tiles_n, tm, tn);
+    int lo, hi;
+    group_range(g.group_off, grp, g.K, lo, hi);
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    hi = __builtin_amdgcn_readfirstlane(hi);
+    Ag += (int64_t)lo * g.lda;
+    Bg += (int64_t)lo * g.ldb;
+    Kg = hi - lo;
+    goff = (int64_t)grp * g.group_stride_c;
+    r0 = tm * T::BM;
+    m_end = g.M;
+  }
 
   f32x16 acc[T::FM][T::FN];
 #pragma unroll
@@ -349,13 +449,12 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
 
   // K-major operands: descriptors based at the tile's first row, fixed for
   // the whole K loop.  MN-major: rebased at every stage's first k-row.
-  const int nk = (g.K + T::BK - 1) / T::BK;
-  i32x4 ra =
-      A_K ? make_rsrc(g.A + (int64_t)tm * T::BM * g.lda, ((int64_t)g.M - (int64_t)tm * T::BM) * g.lda * 2)
-          : make_rsrc(g.A, 0);
+  const int nk = (Kg + T::BK - 1) / T::BK;
+  i32x4 ra = A_K ? make_rsrc(Ag + (int64_t)r0 * g.lda, ((int64_t)m_end - (int64_t)r0) * g.lda * 2)
+                 : make_rsrc(Ag, 0);
   i32x4 rb =
-      B_K ? make_rsrc(g.B + (int64_t)tn * T::BN * g.ldb, ((int64_t)g.N - (int64_t)tn * T::BN) * g.ldb * 2)
-          : make_rsrc(g.B, 0);
+      B_K ? make_rsrc(Bg + (int64_t)tn * T::BN * g.ldb, ((int64_t)g.N - (int64_t)tn * T::BN) * g.ldb * 2)
+          : make_rsrc(Bg, 0);
 
   // Software pipeline.
   //  * Global -> LDS: ring of SA = 3 A buffers and SB = 2 B buffers (160 KB
@@ -383,11 +482,11 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   // descriptors: K-major fixed, MN-major rebased at the stage's first k-row
   auto rs_a = [&](int j) -> i32x4 {
     if constexpr (A_K) return ra;
-    else return make_rsrc(g.A + (int64_t)j * T::BK * g.lda, ((int64_t)g.K - (int64_t)j * T::BK) * g.lda * 2);
+    else return make_rsrc(Ag + (int64_t)j * T::BK * g.lda, ((int64_t)Kg - (int64_t)j * T::BK) * g.lda * 2);
   };
   auto rs_b = [&](int j) -> i32x4 {
     if constexpr (B_K) return rb;
-    else return make_rsrc(g.B + (int64_t)j * T::BK * g.ldb, ((int64_t)g.K - (int64_t)j * T::BK) * g.ldb * 2);
+    else return make_rsrc(Bg + (int64_t)j * T::BK * g.ldb, ((int64_t)Kg - (int64_t)j * T::BK) * g.ldb * 2);
   };
   // this wave loads blocks wave + 4i; their swizzle classes alternate
   // between those of blocks wave and wave + 4 (K-major) or are all equal
@@ -446,7 +545,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
     const SWG_LDS char* as = a_ptr(kt);
     const SWG_LDS char* bs = b_ptr(kt);
     // the epilogue's first global reads go out under the last stage's MFMAs
-    if (kt + 1 == nk) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, tm, tn, 0, g.M, g.N}, pf[0], tid);
+    if (kt + 1 == nk) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, r0, tn, 0, m_end, g.N, goff}, pf[0], tid);
     // steps 0 and 1: A(kt+2), half in each (A(2) came with the prologue)
     const bool load_a_now = kt >= 1 && kt + 2 < nk;
     const i32x4 rA = rs_a(kt + 2);
@@ -479,15 +578,15 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   // flight now are the epilogue prefetches, which must stay in flight: the
   // barriers below are bare s_barriers, not __syncthreads() (whose fence
   // would wait for them).
-  if (nk == 0) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, tm, tn, 0, g.M, g.N}, pf[0], tid);
+  if (nk == 0) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, r0, tn, 0, m_end, g.N, goff}, pf[0], tid);
   barrier();
 
   // ---- epilogue: one 32-row slab per wave row at a time through LDS; the
   // global reads of slab s+PD-1 are issued before slab s is processed ----
   SWG_LDS float* slab = (SWG_LDS float*)smem;
-  SlabCtx<T> ctx{slab, tm, tn, 0, g.M, g.N};
+  SlabCtx<T> ctx{slab, r0, tn, 0, m_end, g.N, goff};
 #pragma unroll
-  for (int s = 1; s + 1 < PD; ++s) Epi::template prefetch<T>(ep, SlabCtx<T>{slab, tm, tn, s, g.M, g.N}, pf[s], tid);
+  for (int s = 1; s + 1 < PD; ++s) Epi::template prefetch<T>(ep, SlabCtx<T>{slab, r0, tn, s, m_end, g.N, goff}, pf[s], tid);
 #pragma unroll
   for (int s = 0; s < T::FM; ++s) {
     ctx.s = s;
@@ -503,7 +602,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
       }
     // after the accumulator writes, whose staging registers are then free
     if (s + PD - 1 < T::FM && PD > 1)
-      Epi::template prefetch<T>(ep, SlabCtx<T>{slab, tm, tn, s + PD - 1, g.M, g.N}, pf[(s + PD - 1) % PD], tid);
+      Epi::template prefetch<T>(ep, SlabCtx<T>{slab, r0, tn, s + PD - 1, m_end, g.N, goff}, pf[(s + PD - 1) % PD], tid);
     barrier();
     Epi::template apply<T>(ep, ctx, pf[s % PD], tid);
   }
@@ -534,7 +633,7 @@ struct EpiStore {
       const int row = c.row(sr), col = c.tn * T::BN + ch * 8;
       if (row < c.M && col < c.N) {
         u32x4 v = pack8(c.read8(sr, ch * 8));
-        *(u32x4*)(p.C + (int64_t)row * p.ldc + col) = v;
+        *(u32x4*)(p.C + c.goff + (int64_t)row * p.ldc + col) = v;
       }
     }
   }

@@ -104,13 +104,13 @@ struct EpiSwigluBwdT {
   __device__ static void prefetch(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
     constexpr int CPR = T::BN / 8;
     const int I = (int)p.I;
-    const char* base = (const char*)(p.preact + (int64_t)c.tm * T::BM * 2 * p.I);
+    const char* base = (const char*)(p.preact + (int64_t)c.r0 * 2 * p.I);
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
       const int row = c.row(sr);
-      const int rl = row - c.tm * T::BM;
+      const int rl = row - c.r0;
       const uint32_t off = (uint32_t)(rl * 2 * I + c.tn * T::BN + ch * 8) * 2u;
       if (row < c.M) {
         pf.left[k] = __builtin_nontemporal_load((const u32x4*)(base + off));
@@ -122,14 +122,14 @@ struct EpiSwigluBwdT {
   __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
     constexpr int CPR = T::BN / 8;
     const int I = (int)p.I;
-    char* gbase = (char*)(p.grad_preact + (int64_t)c.tm * T::BM * 2 * p.I);
-    char* hbase = STORE_H ? (char*)(p.h + (int64_t)c.tm * T::BM * p.I) : nullptr;
+    char* gbase = (char*)(p.grad_preact + (int64_t)c.r0 * 2 * p.I);
+    char* hbase = STORE_H ? (char*)(p.h + (int64_t)c.r0 * p.I) : nullptr;
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
       const int row = c.row(sr);
-      const int rl = row - c.tm * T::BM;
+      const int rl = row - c.r0;
       const int col = c.tn * T::BN + ch * 8;
       if (row < c.M) {
         const f32x8 dout = c.read8(sr, ch * 8);
@@ -276,7 +276,7 @@ int launch_status() { return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGL
 template <class T, bool A_K, bool B_K, class Epi>
 int run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
              int pair_off, const typename Epi::Params& ep, hipStream_t st) {
-  GemmArgs g;
+  GemmArgs g{};
   g.A = A;
   g.B = B;
   g.lda = lda;
@@ -455,6 +455,112 @@ int step_dw1(const void* x, const void* gp, void* dW1, int64_t M, int64_t D, int
   return run_gemm_auto<false, false, EpiStore>(cu16(x), D, cu16(gp), 2 * I, D, 2 * I, M, 0, ep, st);
 }
 
+// --- grouped GEMMs: the experts of a mixture-of-experts layer (Lesson 24,
+// sections 41-43).  Token rows are packed by expert; offsets [E + 1] live in
+// device memory, so routing needs no host round trip: every workgroup finds
+// its expert on the device. ----------------------------------------------
+
+template <class T, bool A_K, bool B_K, class Epi, int GRP>
+int run_gemm_grouped(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N,
+                     int64_t K, int pair_off, const int* off, int64_t E, int64_t stride_b, int64_t stride_c,
+                     const typename Epi::Params& ep, hipStream_t st) {
+  GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.tiles_n = pair_off > 0 ? (int)(N / T::BN) : (int)((N + T::BN - 1) / T::BN);
+  g.pair_off = pair_off;
+  g.group_off = off;
+  g.groups = (int)E;
+  g.group_stride_b = stride_b;
+  g.group_stride_c = stride_c;
+  int64_t tiles;
+  if (GRP == kGroupM) {
+    // each group adds at most one partly filled tile row
+    const int64_t rows = (M + T::BM - 1) / T::BM + E;
+    g.tiles_m = (int)rows;
+    tiles = rows * g.tiles_n;
+  } else {
+    g.tiles_m = (int)((M + T::BM - 1) / T::BM);
+    tiles = E * g.tiles_m * g.tiles_n;
+  }
+  if (tiles == 0) return SWIGLU_OK;
+  if (tiles > 0x7FFFFFFFll) return SWIGLU_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((gemm_kernel<T, A_K, B_K, Epi, GRP>), dim3((unsigned)tiles), dim3(T::THREADS), 0, st, g, ep);
+  return launch_status();
+}
+
+// Tile choice as for one GEMM, with the rows per expert (grouped over M) or
+// the output rows (grouped over K) in the role of M.
+template <bool A_K, bool B_K, class Epi, int GRP>
+int run_grouped_auto(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                     int pair_off, const int* off, int64_t E, int64_t stride_b, int64_t stride_c,
+                     const typename Epi::Params& ep, hipStream_t st) {
+  const int64_t n_unit = pair_off > 0 ? N / 2 : N;
+  const int64_t div = pair_off > 0 ? 2 : 1;
+  const int64_t rows = GRP == kGroupM ? M / E : M;
+  if (n_unit % (TBig::BN / div) == 0 && rows > 256)
+    return run_gemm_grouped<TBig, A_K, B_K, Epi, GRP>(A, lda, B, ldb, M, N, K, pair_off, off, E, stride_b, stride_c,
+                                                      ep, st);
+  if (n_unit % (TMid::BN / div) == 0)
+    return run_gemm_grouped<TMid, A_K, B_K, Epi, GRP>(A, lda, B, ldb, M, N, K, pair_off, off, E, stride_b, stride_c,
+                                                      ep, st);
+  return run_gemm_grouped<TSmall, A_K, B_K, Epi, GRP>(A, lda, B, ldb, M, N, K, pair_off, off, E, stride_b, stride_c,
+                                                      ep, st);
+}
+
+// The six GEMMs of the expert MLP block, each one launch over all experts.
+// M is the routed row count; W1 [E, D, 2I], W_down [E, I, Dout].
+int moe_gemm1(const void* x, const void* W1, const int* off, void* preact, void* h, int64_t M, int64_t D, int64_t I,
+              int64_t E, hipStream_t st) {
+  EpiSwigluFwd::Params ep{u16(preact), u16(h), I};
+  return run_grouped_auto<true, false, EpiSwigluFwd, kGroupM>(cu16(x), D, cu16(W1), 2 * I, M, 2 * I, D, (int)I, off, E,
+                                                               D * 2 * I, 0, ep, st);
+}
+
+int moe_down(const void* h, const void* Wd, const int* off, void* y, int64_t M, int64_t I, int64_t Dout, int64_t E,
+             hipStream_t st) {
+  EpiStore::Params ep{u16(y), Dout};
+  return run_grouped_auto<true, false, EpiStore, kGroupM>(cu16(h), I, cu16(Wd), Dout, M, Dout, I, 0, off, E, I * Dout,
+                                                           0, ep, st);
+}
+
+int moe_dgrad_fused(const void* dy, const void* Wd, const int* off, const void* preact, void* gp, void* h, int64_t M,
+                    int64_t I, int64_t Dout, int64_t E, hipStream_t st) {
+  EpiSwigluBwd::Params ep{cu16(preact), u16(gp), u16(h), I};
+  return run_grouped_auto<true, true, EpiSwigluBwd, kGroupM>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, 0, off, E,
+                                                              I * Dout, 0, ep, st);
+}
+
+int moe_dw_down(const void* h, const void* dy, const int* off, void* dWd, int64_t M, int64_t I, int64_t Dout,
+                int64_t E, hipStream_t st) {
+  EpiStore::Params ep{u16(dWd), Dout};
+  return run_grouped_auto<false, false, EpiStore, kGroupK>(cu16(h), I, cu16(dy), Dout, I, Dout, M, 0, off, E, 0,
+                                                            I * Dout, ep, st);
+}
+
+int moe_dx(const void* gp, const void* W1, const int* off, void* dx, int64_t M, int64_t D, int64_t I, int64_t E,
+           hipStream_t st) {
+  EpiStore::Params ep{u16(dx), D};
+  return run_grouped_auto<true, true, EpiStore, kGroupM>(cu16(gp), 2 * I, cu16(W1), 2 * I, M, D, 2 * I, 0, off, E,
+                                                          D * 2 * I, 0, ep, st);
+}
+
+int moe_dw1(const void* x, const void* gp, const int* off, void* dW1, int64_t M, int64_t D, int64_t I, int64_t E,
+            hipStream_t st) {
+  EpiStore::Params ep{u16(dW1), 2 * I};
+  return run_grouped_auto<false, false, EpiStore, kGroupK>(cu16(x), D, cu16(gp), 2 * I, D, 2 * I, M, 0, off, E, 0,
+                                                            D * 2 * I, ep, st);
+}
+
+int check_experts(int64_t E) { return E < 1 ? SWIGLU_ERR_SHAPE : (E > 65536 ? SWIGLU_ERR_UNSUPPORTED : SWIGLU_OK); }
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
 }  // namespace
 
 // ===========================================================================
@@ -476,7 +582,7 @@ const char* swiglu_status_string(int status) {
   }
 }
 
-int swiglu_abi_version(void) { return (1 << 16) | 2; }
+int swiglu_abi_version(void) { return (1 << 16) | 3; }
 
 size_t swiglu_mlp_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
   if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
@@ -636,6 +742,87 @@ int swiglu_bwd_dx_residual(const void* grad_preact, const void* W1, const void* 
   const Range outs[] = {rng(dx, M * D * 2)};
   SW_TRY(check_alias(ins, 3, outs, 1));
   return step_dx_residual(grad_preact, W1, dy, dx, M, D, I, as_stream(stream));
+}
+
+// --- mixture-of-experts MLP blocks (Lesson 24, sections 41-43) -------------
+
+size_t swiglu_moe_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout, int64_t E) {
+  if (check_dims(M, D, I, Dout) != SWIGLU_OK || check_experts(E) != SWIGLU_OK) return 0;
+  return (size_t)(M * I * 2);
+}
+
+size_t swiglu_moe_bwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout, int64_t E) {
+  if (check_dims(M, D, I, Dout) != SWIGLU_OK || check_experts(E) != SWIGLU_OK) return 0;
+  return align256((size_t)(M * 2 * I * 2)) + align256((size_t)(M * I * 2));
+}
+
+int swiglu_moe_fwd(const void* x, const void* W1, const void* W_down, const int32_t* group_offsets, void* preact,
+                   void* y, void* ws, size_t ws_bytes, int64_t M, int64_t D, int64_t I, int64_t Dout, int64_t E,
+                   void* stream) {
+  SW_TRY(check_dims(M, D, I, Dout));
+  SW_TRY(check_experts(E));
+  if (missing(x, M * D) || !W1 || !W_down || !group_offsets || missing(preact, M * I) || missing(y, M * Dout))
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned4(group_offsets) || !aligned16(preact) ||
+      !aligned16(y) || (ws && !aligned16(ws)))
+    return SWIGLU_ERR_ALIGN;
+  const size_t need = swiglu_moe_fwd_workspace(M, D, I, Dout, E);
+  if (need > 0 && (!ws || ws_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, E * D * 2 * I * 2), rng(W_down, E * I * Dout * 2),
+                       rng(group_offsets, (E + 1) * 4)};
+  const Range outs[] = {rng(preact, M * 2 * I * 2), rng(y, M * Dout * 2), rng(ws, (int64_t)need)};
+  SW_TRY(check_alias(ins, 4, outs, 3));
+  hipStream_t st = as_stream(stream);
+  SW_TRY(moe_gemm1(x, W1, group_offsets, preact, ws, M, D, I, E, st));
+  return moe_down(ws, W_down, group_offsets, y, M, I, Dout, E, st);
+}
+
+int swiglu_moe_bwd(const void* x, const void* W1, const void* W_down, const int32_t* group_offsets,
+                   const void* preact, const void* dy, void* dx, void* dW1, void* dW_down, void* ws, size_t ws_bytes,
+                   int64_t M, int64_t D, int64_t I, int64_t Dout, int64_t E, void* stream) {
+  SW_TRY(check_dims(M, D, I, Dout));
+  SW_TRY(check_experts(E));
+  if (missing(x, M * D) || !W1 || !W_down || !group_offsets || missing(preact, M * I) || missing(dy, M * Dout) ||
+      missing(dx, M * D) || !dW1 || !dW_down)
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned4(group_offsets) || !aligned16(preact) ||
+      !aligned16(dy) || !aligned16(dx) || !aligned16(dW1) || !aligned16(dW_down) || (ws && !aligned16(ws)))
+    return SWIGLU_ERR_ALIGN;
+  const size_t need = swiglu_moe_bwd_workspace(M, D, I, Dout, E);
+  if (need > 0 && (!ws || ws_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, E * D * 2 * I * 2), rng(W_down, E * I * Dout * 2),
+                       rng(group_offsets, (E + 1) * 4), rng(preact, M * 2 * I * 2), rng(dy, M * Dout * 2)};
+  const Range outs[] = {rng(dx, M * D * 2), rng(dW1, E * D * 2 * I * 2), rng(dW_down, E * I * Dout * 2),
+                        rng(ws, (int64_t)need)};
+  SW_TRY(check_alias(ins, 6, outs, 4));
+  hipStream_t st = as_stream(stream);
+  char* w = (char*)ws;
+  void* gp = w;
+  void* h = w + align256((size_t)(M * 2 * I * 2));
+  SW_TRY(moe_dgrad_fused(dy, W_down, group_offsets, preact, gp, h, M, I, Dout, E, st));
+  SW_TRY(moe_dw_down(h, dy, group_offsets, dW_down, M, I, Dout, E, st));
+  SW_TRY(moe_dx(gp, W1, group_offsets, dx, M, D, I, E, st));
+  return moe_dw1(x, gp, group_offsets, dW1, M, D, I, E, st);
+}
+
+int swiglu_moe_bwd_dgrad_fused(const void* dy, const void* W_down, const int32_t* group_offsets, const void* preact,
+                               void* grad_preact, void* h, int64_t M, int64_t I, int64_t Dout, int64_t E,
+                               void* stream) {
+  SW_TRY(check_tokens(M));
+  SW_TRY(check_inner(I));
+  SW_TRY(check_inner(Dout));
+  SW_TRY(check_experts(E));
+  if (missing(dy, M * Dout) || !W_down || !group_offsets || missing(preact, M * I) || missing(grad_preact, M * I) ||
+      missing(h, M * I))
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(dy) || !aligned16(W_down) || !aligned4(group_offsets) || !aligned16(preact) ||
+      !aligned16(grad_preact) || !aligned16(h))
+    return SWIGLU_ERR_ALIGN;
+  const Range ins[] = {rng(dy, M * Dout * 2), rng(W_down, E * I * Dout * 2), rng(group_offsets, (E + 1) * 4),
+                       rng(preact, M * 2 * I * 2)};
+  const Range outs[] = {rng(grad_preact, M * 2 * I * 2), rng(h, M * I * 2)};
+  SW_TRY(check_alias(ins, 4, outs, 2));
+  return moe_dgrad_fused(dy, W_down, group_offsets, preact, grad_preact, h, M, I, Dout, E, as_stream(stream));
 }
 
 // --- save-h fallback (the drop-h report's normal MLPBlock) ------------------

@@ -67,7 +67,7 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* swiglu_status_string(int status);
 
-/* ABI version of this header, (major << 16) | minor: 1.2. */
+/* ABI version of this header, (major << 16) | minor: 1.3. */
 int swiglu_abi_version(void);
 
 /* ---------------------------------------------------------------------------
@@ -169,6 +169,58 @@ int swiglu_mlp_bwd_residual(const void* x, const void* W1, const void* W_down, c
                             void* dx, void* dW1, void* dW_down,
                             void* ws, size_t ws_bytes,
                             int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Mixture-of-experts MLP blocks (Lesson 24, section 41: each expert is its
+ * own SwiGLU MLP; sections 42-43: one grouped GEMM launch serves all experts
+ * whatever their token counts).  The routed token rows arrive sorted and
+ * packed by expert: expert e owns rows [group_offsets[e], group_offsets[e+1])
+ * of x, preact, dy and dx.  Routing, sorting and All-to-All are the caller's.
+ *
+ * group_offsets: int32 [E + 1] in DEVICE memory (4-byte aligned), read by the
+ * kernels, so the host never waits for the router.  It must run from 0 to M
+ * without decreasing.  The host cannot check its contents: offsets outside
+ * [0, M] are clamped and a decreasing pair makes that expert empty, so a bad
+ * table gives unspecified results but no access outside the tensors.
+ * Weights: W1 [E, D, 2I] and W_down [E, I, Dout], one block per expert, each
+ * laid out as the dense block's.  1 <= E <= 65536 (else SWIGLU_ERR_SHAPE /
+ * SWIGLU_ERR_UNSUPPORTED).  An expert with no rows gets zero weight
+ * gradients.  The saved set for the backward is {x, W1, W_down,
+ * group_offsets, preact}; h is recomputed as in swiglu_mlp_bwd.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace swiglu_moe_fwd needs: the transient h [M,I].
+ * Returns 0 for invalid arguments. */
+size_t swiglu_moe_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout, int64_t E);
+
+/* Bytes of device workspace swiglu_moe_bwd needs: grad_preact [M,2I] and h
+ * [M,I].  Returns 0 for invalid arguments. */
+size_t swiglu_moe_bwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout, int64_t E);
+
+/* Forward of all experts: two grouped launches (GEMM-1 with the SwiGLU
+ * epilogue, then the down GEMM).  x [M,D] -> preact [M,2I], y [M,Dout]. */
+int swiglu_moe_fwd(const void* x, const void* W1, const void* W_down, const int32_t* group_offsets,
+                   void* preact, void* y,
+                   void* ws, size_t ws_bytes,
+                   int64_t M, int64_t D, int64_t I, int64_t Dout, int64_t E, void* stream);
+
+/* Backward of all experts: the grouped fused dgrad (dout per expert stays on
+ * chip; the epilogue writes grad_preact and h to ws), then dW_down [E,I,Dout]
+ * and dW1 [E,D,2I] as GEMMs grouped over the token (reduction) dimension, and
+ * dx [M,D] grouped over rows.  Four launches. */
+int swiglu_moe_bwd(const void* x, const void* W1, const void* W_down, const int32_t* group_offsets,
+                   const void* preact, const void* dy,
+                   void* dx, void* dW1, void* dW_down,
+                   void* ws, size_t ws_bytes,
+                   int64_t M, int64_t D, int64_t I, int64_t Dout, int64_t E, void* stream);
+
+/* The grouped fused dgrad step alone (one launch): per expert e,
+ * dout = dy_e . W_down[e]^T kept in fp32, and the epilogue of
+ * swiglu_bwd_dgrad_fused.  dy [M,Dout], W_down [E,I,Dout], preact [M,2I] ->
+ * grad_preact [M,2I], h [M,I]. */
+int swiglu_moe_bwd_dgrad_fused(const void* dy, const void* W_down, const int32_t* group_offsets,
+                               const void* preact, void* grad_preact, void* h,
+                               int64_t M, int64_t I, int64_t Dout, int64_t E, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Single steps (each is one kernel launch; used by the whole-step calls

@@ -132,7 +132,6 @@ def test_save_h_entry_points_reject_bad_arguments():
     a = [addr(i) for i in range(11)]
     M, D, I, Dout = 128, 256, 512, 256
     fwd = lambda *p: L.swiglu_mlp_fwd_save_h(*p, M, D, I, Dout, None)
-    assert fwd(*a[:6]) is not None
     assert fwd(None, *a[1:6]) == NULL
     assert fwd(*a[:4], None, a[5]) == NULL                  # h is required
     assert fwd(*a[:4], a[4] + 8, a[5]) == ALIGN
@@ -187,6 +186,53 @@ def test_residual_entry_points_reject_bad_arguments():
     assert L.swiglu_bwd_dx_residual(a[0], a[1], a[2], a[2], M, D, I, None) == ALIAS
     assert L.swiglu_bwd_dx_residual(a[0], a[1], None, a[3], M, D, I, None) == NULL
     assert L.swiglu_bwd_dx_residual(a[0], a[1], a[2], a[3], -1, D, I, None) == SHAPE
+
+
+def test_moe_entry_points_reject_bad_arguments():
+    L = sw.lib()
+    M, D, I, Dout, E = 300, 256, 512, 256, 8
+    assert L.swiglu_moe_fwd_workspace(M, D, I, Dout, E) == M * I * 2
+    assert L.swiglu_moe_bwd_workspace(M, D, I, Dout, E) == L.swiglu_mlp_bwd_workspace(M, D, I, Dout)
+    assert L.swiglu_moe_fwd_workspace(M, D, I, Dout, 0) == 0
+    assert L.swiglu_moe_bwd_workspace(M, 100, I, Dout, E) == 0
+    fwd = lambda p, E=E, wsb=1 << 40: L.swiglu_moe_fwd(*p[:6], p[6], wsb, M, D, I, Dout, E, None)
+    p = [addr(i) for i in range(7)]
+    assert fwd(p, E=0) == SHAPE
+    assert fwd(p, E=65537) == UNSUP
+    for k in range(6):
+        q = list(p); q[k] = None
+        assert fwd(q) == NULL, k
+    q = list(p); q[3] = p[3] + 2                              # offsets need 4-byte alignment
+    assert fwd(q) == ALIGN
+    q = list(p); q[3] = p[3] + 4                              # 4 bytes suffice: the next check refuses
+    assert fwd(q, wsb=10) == WS
+    assert fwd(p, wsb=10) == WS
+    q = list(p); q[4] = addr(3)                               # preact onto the offsets
+    assert fwd(q) == ALIAS
+    q = list(p); q[5] = p[1] + 2 * (D * 2 * I * 2)            # y inside expert 2's W1
+    assert fwd(q) == ALIAS
+    bwd = lambda p, E=E, wsb=1 << 40: L.swiglu_moe_bwd(*p[:9], p[9], wsb, M, D, I, Dout, E, None)
+    p = [addr(i) for i in range(10)]
+    for k in range(9):
+        q = list(p); q[k] = None
+        assert bwd(q) == NULL, k
+    assert bwd(p, wsb=10) == WS
+    q = list(p); q[7] = p[2] + 16                             # dW1 overlapping W_down
+    assert bwd(q) == ALIAS
+    assert bwd(p, E=-1) == SHAPE
+    g = lambda *a: L.swiglu_moe_bwd_dgrad_fused(*a)
+    a = [addr(i) for i in range(6)]
+    assert g(a[0], a[1], a[2], a[3], a[3], a[5], M, I, Dout, E, None) == ALIAS
+    assert g(a[0], a[1], None, a[3], a[4], a[5], M, I, Dout, E, None) == NULL
+    assert g(a[0], a[1], a[2], a[3], a[4], a[5], M, 100, Dout, E, None) == UNSUP
+
+
+def test_moe_binding_checks_offsets_on_the_host():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sw.swiglu_moe_fwd(x, torch.zeros(2, 64, 128, dtype=torch.bfloat16), torch.zeros(2, 64, 64, dtype=torch.bfloat16),
+                          torch.zeros(3, dtype=torch.int32))
 
 
 def test_python_binding_refuses_cpu_tensors():
