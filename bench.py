@@ -100,6 +100,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         return copy_calibration()
+    from workload import MOE_WORKLOADS
+    if args.workload in MOE_WORKLOADS:
+        return bench_moe(args, MOE_WORKLOADS[args.workload])
     w = WORKLOADS[args.workload]
     if w.fwd_only:
         return bench_decode(args, w)
@@ -446,6 +449,145 @@ def bench_decode(args, w):
         "fwd_us": round(ms * 1e3, 2),
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_moe(args, w):
+    """Mixture-of-experts block (expert MLPs over expert-packed rows): the
+    grouped fused dgrad's TFLOP/s (one launch for all experts), the whole
+    block's forward and backward, and paired A/B of the grouped launches
+    against the same work as one dense launch per expert."""
+    import torch
+    import bwd_gemm_epilogue_amd as sw
+    from workload import make_moe_inputs
+    dev = torch.device("cuda:0")
+
+    def to_dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.time()
+    xb, W1b, Wdb, dyb, offb = make_moe_inputs(w, weight_sets=2)
+    x, W1, Wd, dy = (to_dev(a) for a in (xb, W1b, Wdb, dyb))
+    off = torch.from_numpy(offb).to(dev)
+    M, D, I, Dout, E = int(offb[-1]), w.D, w.I, w.Dout, w.experts
+    counts = np.diff(offb)
+    print(f"[bench] moe inputs {M}x{D}x{I}x{Dout}, {E} experts (rows {counts.min()}..{counts.max()}) "
+          f"ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    bf = torch.bfloat16
+    preact = torch.empty((M, 2 * I), dtype=bf, device=dev)
+    y = torch.empty((M, Dout), dtype=bf, device=dev)
+    dx = torch.empty((M, D), dtype=bf, device=dev)
+    dW1 = torch.empty((E, D, 2 * I), dtype=bf, device=dev)
+    dWd = torch.empty((E, I, Dout), dtype=bf, device=dev)
+    gp = torch.empty((M, 2 * I), dtype=bf, device=dev)
+    h = torch.empty((M, I), dtype=bf, device=dev)
+    wsf = torch.empty(max(1, sw.swiglu_moe_fwd_workspace(M, D, I, Dout, E)), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(1, sw.swiglu_moe_bwd_workspace(M, D, I, Dout, E)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sl = [(int(offb[e]), int(offb[e + 1])) for e in range(E)]
+
+    def fwd():
+        sw.swiglu_moe_fwd(x, W1, Wd, off, preact, y, wsf)
+
+    def bwd():
+        sw.swiglu_moe_bwd(x, W1, Wd, off, preact, dy, dx, dW1, dWd, wsb)
+
+    def b1_grouped():
+        sw.swiglu_moe_bwd_dgrad_fused(dy, Wd, off, preact, gp, h)
+
+    def b1_per_expert():
+        for e, (a, b) in enumerate(sl):
+            sw.swiglu_bwd_dgrad_fused(dy[a:b], Wd[e], preact[a:b], gp[a:b], h[a:b])
+
+    def step_per_expert():
+        for e, (a, b) in enumerate(sl):
+            sw.swiglu_mlp_fwd(x[a:b], W1[e], Wd[e], preact[a:b], y[a:b])
+        for e, (a, b) in enumerate(sl):
+            sw.swiglu_mlp_bwd(x[a:b], W1[e], Wd[e], preact[a:b], dy[a:b], dx[a:b], dW1[e], dWd[e])
+
+    for _ in range(args.warmup):
+        fwd(); bwd(); b1_grouped()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t1 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        fwd()
+        ev[k][1].record(stream)
+        bwd()
+        ev[k][2].record(stream)
+        b1_grouped()
+        ev[k][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    b1_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    b1_flops = 2 * M * Dout * I
+    b1_tflops = b1_flops / (b1_ms * 1e-3) / 1e12
+    step_flops = 3 * (4 * M * D * I + 2 * M * I * Dout)  # forward 4MDI + 2MIDout, backward twice that
+
+    # paired A/B: grouped launches against one dense launch per expert
+    def pairs(fa, fb, n):
+        ta, tb = [], []
+        e3 = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for _ in range(n):
+            e3[0].record(stream); fa(); e3[1].record(stream); fb(); e3[2].record(stream)
+            torch.cuda.synchronize()
+            ta.append(e3[0].elapsed_time(e3[1])); tb.append(e3[1].elapsed_time(e3[2]))
+        return float(np.median(ta)), float(np.median(tb))
+
+    g_b1, d_b1 = pairs(b1_grouped, b1_per_expert, 10)
+    g_st, d_st = pairs(lambda: (fwd(), bwd()), step_per_expert, 6)
+    cpu = cpu_baseline_moe(w, xb, W1b, Wdb, dyb, offb, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    out = {
+        "metric": "grouped fused dout-GEMM+SwiGLU-bwd TFLOP/s over all experts; MoE block fwd+bwd ms",
+        "value": round(b1_tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name} mixture-of-experts SwiGLU block fwd+bwd", "routed_rows": M, "D": D,
+                   "I": I, "Dout": Dout, "experts": E, "top_k": w.top_k, "tokens": w.tokens,
+                   "rows_per_expert_min_max": [int(counts.min()), int(counts.max())],
+                   "distinct_expert_weight_sets": 2},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "step_tflops": round(step_flops / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2),
+        "ab_grouped_vs_per_expert": {
+            "dgrad_fused_grouped_ms": round(g_b1, 4), "dgrad_fused_per_expert_ms": round(d_b1, 4),
+            "step_grouped_ms": round(g_st, 4), "step_per_expert_ms": round(d_st, 4),
+            "launches_grouped": 6, "launches_per_expert": 6 * E},
+        "roofline": {"kernel": "grouped bwd_dgrad_fused", "bound": "mfma", "achieved": round(b1_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(b1_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(f"dgrad_fused_{w.name}"),
+                     "algorithmic_flops_per_launch": b1_flops,
+                     "algorithmic_bytes_per_launch": 2 * (M * Dout + E * I * Dout + 2 * M * 2 * I + M * I)},
+        "cpu_baseline": cpu,
+        "kernel_source_digest": source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_moe(w, xb, W1b, Wdb, dyb, offb, budget_s):
+    """The fp64 oracle of the fused dgrad step, expert by expert, over the
+    first experts' rows until the time budget is spent, scaled to TFLOP/s."""
+    import oracle
+    from workload import bf16_bits_to_f64
+    t_total, rows, experts = 0.0, 0, 0
+    for e in range(w.experts):
+        a, b = int(offb[e]), int(offb[e + 1])
+        if a == b:
+            continue
+        pre = bf16_bits_to_f64(xb[a:b]) @ bf16_bits_to_f64(W1b[e])     # setup: the saved preact
+        dyr, Wd = bf16_bits_to_f64(dyb[a:b]), bf16_bits_to_f64(Wdb[e])
+        t = time.perf_counter()
+        oracle.swiglu_bwd_elementwise(pre, dyr @ Wd.T)
+        t_total += time.perf_counter() - t
+        rows += b - a
+        experts += 1
+        if t_total > budget_s:
+            break
+    fl = 2 * rows * w.Dout * w.I
+    return {"value": round(fl / t_total / 1e12, 5), "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"fused dgrad step of the first {experts} experts ({rows} of {int(offb[-1])} routed rows), "
+                      f"fp64 numpy, {t_total:.1f}s"}
 
 
 if __name__ == "__main__":
