@@ -93,6 +93,26 @@ def test_moe_vs_oracle_and_dense(name, counts, dims):
         assert np.array_equal(bits(a), bits(b)), n
 
 
+@pytest.mark.parametrize("E", [64, 65, 150])
+def test_moe_many_experts(E):
+    """More experts than one wave scans at once (64 per pass): the device-side
+    lookup walks several 64-expert chunks, with runs of empty experts."""
+    print("case: moe experts", E, flush=True)
+    rng = np.random.default_rng(E)
+    counts = rng.integers(0, 12, E) * (rng.random(E) < 0.6)
+    counts[-1] = max(int(counts[-1]), 3)          # rows in the last chunk
+    xb, W1b, Wdb, dyb, off = _custom(list(counts), 128, 128, 128, seed=59)
+    x, W1, Wd, dy, offd = _dev_inputs(xb, W1b, Wdb, dyb, off)
+    pre, y = sw.swiglu_moe_fwd(x, W1, Wd, offd)
+    dx, dW1, dWd = sw.swiglu_moe_bwd(x, W1, Wd, offd, pre, dy)
+    torch.cuda.synchronize()
+    _check_vs_oracle(xb, W1b, Wdb, dyb, off, pre, y, dx, dW1, dWd)
+    ref = _dense_per_expert(x, W1, Wd, dy, off)
+    torch.cuda.synchronize()
+    for a, b, n in zip((pre, y, dx, dW1, dWd), ref, ("preact", "y", "dx", "dW1", "dW_down")):
+        assert np.array_equal(bits(a), bits(b)), n
+
+
 def test_moe_dgrad_step_and_degenerate_tables():
     print("case: moe dgrad step, empty batch, everything in the last expert", flush=True)
     xb, W1b, Wdb, dyb, off = _custom([40, 0, 97], 256, 512, 256, seed=55)
