@@ -15,13 +15,16 @@
  * silu' forms; sections 3-4 the fused dout-GEMM epilogue), the "SwiGLU MLP
  * Drop-H technical report" (forward/backward formulas, the saved set
  * {x, W1, W2, preact}, h dropped after the down projection, non-inplace
- * backward that allocates h and grad_preact), and "Lesson 24" section 11
- * (sigma and SiLU definitions).
+ * backward that allocates h and grad_preact; its save-h fallback), and
+ * "Lesson 24" (section 11 sigma and SiLU; section 24 the residual-add
+ * epilogue; sections 41-43 mixture-of-experts MLPs and the grouped GEMM).
  *
  * Conventions for every entry point below:
  *   - Tensor arguments are DEVICE pointers to bf16 values (raw 16-bit
  *     patterns), row-major and densely packed (leading dimension = number
- *     of columns), owned by the caller.  Each must be 16-byte aligned.
+ *     of columns), owned by the caller.  Each must be 16-byte aligned.  The
+ *     one exception is the int32 expert-offset table of the mixture-of-
+ *     experts calls (4-byte aligned).
  *   - W1 is [D, 2I]: columns [0, I) are the un-gated "left" (up) branch and
  *     columns [I, 2I) the gate branch.  W_down is [I, Dout].
  *   - Inputs are never written.  Outputs are overwritten (not accumulated).
