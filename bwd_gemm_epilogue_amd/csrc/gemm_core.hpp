@@ -88,10 +88,15 @@ struct GemmArgs {
   const int* group_off;
   int groups;
   int64_t group_stride_b, group_stride_c;
+  // Split tail (kSplitTail): the launch covers tile ids [tile_base,
+  // tile_base + grid / splits) of the tiles_m x tiles_n order, each tile's
+  // K range cut into `splits` parts, one workgroup each.  Dense launches
+  // cover ids [0, tile_count) (tile_count <= tiles_m * tiles_n).
+  int tile_base, tile_count, splits;
 };
 
 // How the kernel maps work to tiles.
-enum GroupMode { kDense = 0, kGroupM = 1, kGroupK = 2 };
+enum GroupMode { kDense = 0, kGroupM = 1, kGroupK = 2, kSplitTail = 3 };
 
 // ---------------------------------------------------------------------------
 // LDS layouts
@@ -411,7 +416,22 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   const uint16_t* Bg = g.B;
   int64_t goff = 0;
   if constexpr (GRP == kDense) {
-    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    tile_order(xcd_linear(blockIdx.x, g.tile_count), g.tiles_m, g.tiles_n, tm, tn);
+    r0 = tm * T::BM;
+    m_end = g.M;
+  } else if constexpr (GRP == kSplitTail) {
+    // workgroup -> (tail tile t, part s); part s takes k-stages
+    // [s * nst / splits, (s + 1) * nst / splits) and writes its fp32 partial
+    // tile to slot t * splits + s of the epilogue's buffer
+    const int t = blockIdx.x / g.splits, sp = blockIdx.x - t * g.splits;
+    tile_order(g.tile_base + t, g.tiles_m, g.tiles_n, tm, tn);
+    const int nst = (g.K + T::BK - 1) / T::BK;
+    const int k0 = sp * nst / g.splits * T::BK;
+    const int k1 = (sp + 1) * nst / g.splits * T::BK;
+    Ag += A_K ? (int64_t)k0 : (int64_t)k0 * g.lda;
+    Bg += B_K ? (int64_t)k0 : (int64_t)k0 * g.ldb;
+    Kg = (k1 < g.K ? k1 : g.K) - k0;
+    goff = (int64_t)blockIdx.x * T::BM * T::BN;
     r0 = tm * T::BM;
     m_end = g.M;
   } else if constexpr (GRP == kGroupM) {
@@ -644,6 +664,66 @@ struct EpiStore {
     }
   }
 };
+
+// ---------------------------------------------------------------------------
+// fp32 partial tile of a split tail: the whole BM x BN tile (rows past M
+// hold zeros from the zero-filled loads) at slot goff of P, row-major with
+// pitch BN.  The split-tail reduce kernel adds a tile's parts in order.
+// ---------------------------------------------------------------------------
+struct EpiPartial {
+  static constexpr int kPrefetchDepth = 1;
+  struct Params {
+    float* P;
+  };
+  template <class T>
+  struct Prefetch {};
+  template <class T>
+  __device__ static void prefetch(const Params&, const SlabCtx<T>&, Prefetch<T>&, int) {}
+  template <class T>
+  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>&, int tid) {
+    constexpr int CPR = T::BN / 8;
+    constexpr int ITEMS = T::SLAB_ROWS * CPR;
+    static_assert(ITEMS % T::THREADS == 0, "slab items must split evenly");
+#pragma unroll
+    for (int k = 0; k < ITEMS / T::THREADS; ++k) {
+      const int it = tid + k * T::THREADS;
+      const int sr = it / CPR, ch = it % CPR;
+      const f32x8 v = c.read8(sr, ch * 8);
+      f32x4* q = (f32x4*)(p.P + c.goff + (int64_t)(c.row(sr) - c.r0) * T::BN + ch * 8);
+      __builtin_nontemporal_store(__builtin_shufflevector(v, v, 0, 1, 2, 3), q);
+      __builtin_nontemporal_store(__builtin_shufflevector(v, v, 4, 5, 6, 7), q + 1);
+    }
+  }
+};
+
+// C = bf16(sum over s < S of the parts of each tail tile), for tile ids
+// [tile_base, tile_base + tiles) of the tiles_m x tiles_n order; one thread
+// per 8 columns of a tile row, BM * BN / 8 / 256 workgroups per tile.
+template <class T>
+__global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restrict__ P, int S, int tile_base,
+                                                           int tiles_m, int tiles_n, int M, int N,
+                                                           uint16_t* __restrict__ C, int64_t ldc) {
+  constexpr int PER_TILE = T::BM * T::BN / 8 / 256;
+  static_assert(PER_TILE * 256 * 8 == T::BM * T::BN, "whole workgroups per tile");
+  const int t = blockIdx.x / PER_TILE;
+  const int it = (blockIdx.x - t * PER_TILE) * 256 + threadIdx.x;
+  const int r = it / (T::BN / 8), c = (it % (T::BN / 8)) * 8;
+  int tm, tn;
+  tile_order(tile_base + t, tiles_m, tiles_n, tm, tn);
+  const int row = tm * T::BM + r, col = tn * T::BN + c;
+  if (row >= M || col >= N) return;
+  f32x8 v = {};
+  for (int s = 0; s < S; ++s) {
+    const f32x4* q = (const f32x4*)(P + ((int64_t)t * S + s) * T::BM * T::BN + r * T::BN + c);
+    const f32x4 lo = __builtin_nontemporal_load(q), hi = __builtin_nontemporal_load(q + 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] += lo[e];
+      v[4 + e] += hi[e];
+    }
+  }
+  *(u32x4*)(C + (int64_t)row * ldc + col) = pack8(v);
+}
 
 // ---------------------------------------------------------------------------
 // Residual-add epilogue ("Lesson 24", section 24): C = bf16(acc + R), the

@@ -288,6 +288,7 @@ int run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int
   g.tiles_n = pair_off > 0 ? (int)(N / T::BN) : (int)((N + T::BN - 1) / T::BN);
   g.pair_off = pair_off;
   const int64_t tiles = (int64_t)g.tiles_m * g.tiles_n;
+  g.tile_count = (int)tiles;
   if (tiles == 0) return SWIGLU_OK;
   hipLaunchKernelGGL((gemm_kernel<T, A_K, B_K, Epi>), dim3((unsigned)tiles), dim3(T::THREADS), 0, st, g, ep);
   return launch_status();
@@ -305,6 +306,99 @@ int run_gemm_auto(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb
   if (n_unit % (TMid::BN / div) == 0)
     return run_gemm<TMid, A_K, B_K, Epi>(A, lda, B, ldb, M, N, K, pair_off, ep, st);
   return run_gemm<TSmall, A_K, B_K, Epi>(A, lda, B, ldb, M, N, K, pair_off, ep, st);
+}
+
+// --- split tail: the last, partly filled round of 256x256 tiles ------------
+// A GEMM of T tiles on C compute units runs floor(T / C) full rounds and a
+// last round of R = T mod C tiles in which most units idle.  When it pays,
+// the R tail tiles have their K range cut into S parts: R * S workgroups
+// write fp32 partial tiles to workspace and a small kernel adds each tile's
+// parts in order.  Plain bf16-store GEMMs only (the sum must be linear);
+// used by the whole-step calls, which own a workspace.
+
+constexpr int kComputeUnits = 256;  // MI355X
+
+struct Scratch {
+  float* p = nullptr;
+  size_t bytes = 0;
+};
+
+struct SplitPlan {
+  int full = 0, rem = 0, S = 1;  // full rounds x units, tail tiles, parts per tail tile
+  size_t bytes = 0;              // partial tiles: rem * S * 256 * 256 * 4
+};
+
+// The plan for a TBig GEMM (N a multiple of 256, M > 256).  The tail's cost
+// in units of one round of tile work, for S parts per tile:
+//   ceil(rem * S / C) / S                     rounds of 1/S-long workgroups
+//   + 2 * rem * S * 256 KB / (5 TB/s)          partial tiles written and read
+//     / (256 * 256 * K * 2 FLOP / 4.5 TFLOP/s)  one tile's main loop on one CU
+// (the two rates are round figures measured on MI355X).  Unsplit, a last
+// round with few busy units runs faster than a full one: its cost is taken
+// as 0.5 + 0.5 * rem / C (measured: 0.72 with 41% of the units busy).  The S
+// in 2..16 (at most the k-stages) of least cost is kept when it saves at
+// least 20% of that.
+SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
+  SplitPlan pl;
+  if (M <= 256 || N % TBig::BN != 0 || K <= 0) return pl;
+  const int64_t tiles = ((M + TBig::BM - 1) / TBig::BM) * (N / TBig::BN);
+  const int64_t full = tiles / kComputeUnits, rem = tiles % kComputeUnits;
+  const int64_t nst = (K + TBig::BK - 1) / TBig::BK;
+  if (full < 1 || rem == 0) return pl;
+  const double tile_bytes = (double)TBig::BM * TBig::BN * 4;
+  const double round_us = 2.0 * TBig::BM * TBig::BN * (double)K / 4.5e6;
+  double best = 1.0;
+  int bestS = 1;
+  for (int S = 2; S <= 16 && S <= nst; ++S) {
+    const double rounds = (double)((rem * S + kComputeUnits - 1) / kComputeUnits) / S;
+    const double traffic_us = 2.0 * rem * S * tile_bytes / 5e6;
+    const double cost = rounds + traffic_us / round_us;
+    if (cost < best - 1e-9) {
+      best = cost;
+      bestS = S;
+    }
+  }
+  const double unsplit = 0.5 + 0.5 * (double)rem / kComputeUnits;
+  if (bestS < 2 || best > 0.8 * unsplit) return pl;
+  pl.full = (int)(full * kComputeUnits);
+  pl.rem = (int)rem;
+  pl.S = bestS;
+  pl.bytes = (size_t)rem * bestS * TBig::BM * TBig::BN * 4;
+  return pl;
+}
+
+// A plain bf16-store GEMM, with the split tail when the plan has one and
+// the scratch holds it; else one dense launch.
+template <bool A_K, bool B_K>
+int run_store_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                   const EpiStore::Params& ep, Scratch sc, hipStream_t st) {
+  const SplitPlan pl = split_plan(M, N, K);
+  if (pl.S < 2 || !sc.p || sc.bytes < pl.bytes)
+    return run_gemm_auto<A_K, B_K, EpiStore>(A, lda, B, ldb, M, N, K, 0, ep, st);
+  typedef TBig T;
+  GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.tiles_m = (int)((M + T::BM - 1) / T::BM);
+  g.tiles_n = (int)(N / T::BN);
+  g.tile_count = pl.full;
+  hipLaunchKernelGGL((gemm_kernel<T, A_K, B_K, EpiStore>), dim3((unsigned)pl.full), dim3(T::THREADS), 0, st, g, ep);
+  SW_TRY(launch_status());
+  g.tile_base = pl.full;
+  g.splits = pl.S;
+  EpiPartial::Params pp{sc.p};
+  hipLaunchKernelGGL((gemm_kernel<T, A_K, B_K, EpiPartial, kSplitTail>), dim3((unsigned)(pl.rem * pl.S)),
+                     dim3(T::THREADS), 0, st, g, pp);
+  SW_TRY(launch_status());
+  constexpr int PER_TILE = T::BM * T::BN / 8 / 256;
+  hipLaunchKernelGGL(split_reduce_kernel<T>, dim3((unsigned)(pl.rem * PER_TILE)), dim3(256), 0, st, (const float*)sc.p,
+                     pl.S, pl.full, g.tiles_m, g.tiles_n, (int)M, (int)N, ep.C, ep.ldc);
+  return launch_status();
 }
 
 // --- decode-shaped forward (at most 16 token rows) -------------------------
@@ -382,9 +476,10 @@ int step_gemm1(const void* x, const void* W1, void* preact, void* h, int64_t M, 
   return run_gemm_auto<true, false, EpiSwigluFwd>(cu16(x), D, cu16(W1), 2 * I, M, 2 * I, D, (int)I, ep, st);
 }
 
-int step_down(const void* h, const void* Wd, void* y, int64_t M, int64_t I, int64_t Dout, hipStream_t st) {
+int step_down(const void* h, const void* Wd, void* y, int64_t M, int64_t I, int64_t Dout, hipStream_t st,
+              Scratch sc = {}) {
   EpiStore::Params ep{u16(y), Dout};
-  return run_gemm_auto<true, false, EpiStore>(cu16(h), I, cu16(Wd), Dout, M, Dout, I, 0, ep, st);
+  return run_store_gemm<true, false>(cu16(h), I, cu16(Wd), Dout, M, Dout, I, ep, sc, st);
 }
 
 int step_dgrad_fused(const void* dy, const void* Wd, const void* preact, void* gp, void* h, int64_t M, int64_t I,
@@ -438,21 +533,35 @@ int step_zero(void* p, int64_t bytes, hipStream_t st) {
   return launch_status();
 }
 
-int step_dw_down(const void* h, const void* dy, void* dWd, int64_t M, int64_t I, int64_t Dout, hipStream_t st) {
+int step_dw_down(const void* h, const void* dy, void* dWd, int64_t M, int64_t I, int64_t Dout, hipStream_t st,
+                 Scratch sc = {}) {
   if (M == 0) return step_zero(dWd, I * Dout * 2, st);
   EpiStore::Params ep{u16(dWd), Dout};
-  return run_gemm_auto<false, false, EpiStore>(cu16(h), I, cu16(dy), Dout, I, Dout, M, 0, ep, st);
+  return run_store_gemm<false, false>(cu16(h), I, cu16(dy), Dout, I, Dout, M, ep, sc, st);
 }
 
-int step_dx(const void* gp, const void* W1, void* dx, int64_t M, int64_t D, int64_t I, hipStream_t st) {
+int step_dx(const void* gp, const void* W1, void* dx, int64_t M, int64_t D, int64_t I, hipStream_t st,
+            Scratch sc = {}) {
   EpiStore::Params ep{u16(dx), D};
-  return run_gemm_auto<true, true, EpiStore>(cu16(gp), 2 * I, cu16(W1), 2 * I, M, D, 2 * I, 0, ep, st);
+  return run_store_gemm<true, true>(cu16(gp), 2 * I, cu16(W1), 2 * I, M, D, 2 * I, ep, sc, st);
 }
 
-int step_dw1(const void* x, const void* gp, void* dW1, int64_t M, int64_t D, int64_t I, hipStream_t st) {
+int step_dw1(const void* x, const void* gp, void* dW1, int64_t M, int64_t D, int64_t I, hipStream_t st,
+             Scratch sc = {}) {
   if (M == 0) return step_zero(dW1, D * 2 * I * 2, st);
   EpiStore::Params ep{u16(dW1), 2 * I};
-  return run_gemm_auto<false, false, EpiStore>(cu16(x), D, cu16(gp), 2 * I, D, 2 * I, M, 0, ep, st);
+  return run_store_gemm<false, false>(cu16(x), D, cu16(gp), 2 * I, D, 2 * I, M, ep, sc, st);
+}
+
+// split-tail scratch of the forward (the down GEMM) and of the backward's
+// plain-store GEMMs (dW_down, dx, dW1 run one after another and share it)
+size_t fwd_split_bytes(int64_t M, int64_t I, int64_t Dout) { return split_plan(M, Dout, I).bytes; }
+size_t bwd_split_bytes(int64_t M, int64_t D, int64_t I, int64_t Dout) {
+  size_t b = split_plan(I, Dout, M).bytes;
+  const size_t c = split_plan(M, D, 2 * I).bytes, d = split_plan(D, 2 * I, M).bytes;
+  if (c > b) b = c;
+  if (d > b) b = d;
+  return b;
 }
 
 // --- grouped GEMMs: the experts of a mixture-of-experts layer (Lesson 24,
@@ -584,15 +693,19 @@ const char* swiglu_status_string(int status) {
 
 int swiglu_abi_version(void) { return (1 << 16) | 3; }
 
+// Workspace layouts (each part 256-byte aligned):
+//   forward          h [M,I] | skinny partial sums or the down GEMM's split tail
+//   backward         grad_preact [M,2I] | h [M,I] | split tail of dW_down, dx, dW1
+//   unfused backward grad_preact | h | dout [M,I] | split tail
 size_t swiglu_mlp_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
   if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
   const size_t h = align256((size_t)(M * I * 2));
-  return fwd_is_skinny(M, I, Dout) ? h + skinny_partial_bytes(D, I, Dout) : h;
+  return fwd_is_skinny(M, I, Dout) ? h + skinny_partial_bytes(D, I, Dout) : h + fwd_split_bytes(M, I, Dout);
 }
 
 size_t swiglu_mlp_bwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
   if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
-  return align256((size_t)(M * 2 * I * 2)) + align256((size_t)(M * I * 2));
+  return align256((size_t)(M * 2 * I * 2)) + align256((size_t)(M * I * 2)) + bwd_split_bytes(M, D, I, Dout);
 }
 
 size_t swiglu_mlp_bwd_unfused_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
@@ -618,7 +731,10 @@ int swiglu_mlp_fwd(const void* x, const void* W1, const void* W_down, void* prea
     return fwd_skinny(x, W1, W_down, preact, y, ws, (float*)((char*)ws + align256((size_t)(M * I * 2))), M, D, I,
                       Dout, st);
   SW_TRY(step_gemm1(x, W1, preact, ws, M, D, I, st));
-  return step_down(ws, W_down, y, M, I, Dout, st);
+  const size_t h_bytes = align256((size_t)(M * I * 2));
+  // the split tail's scratch lies inside the checked [ws, ws + need)
+  const Scratch sc{(float*)((char*)ws + h_bytes), need - h_bytes};
+  return step_down(ws, W_down, y, M, I, Dout, st, sc);
 }
 
 static int bwd_common(bool fused, const void* x, const void* W1, const void* W_down, const void* preact,
@@ -642,16 +758,19 @@ static int bwd_common(bool fused, const void* x, const void* W1, const void* W_d
   char* w = (char*)ws;
   void* gp = w;
   void* h = w + align256((size_t)(M * 2 * I * 2));
+  size_t used = align256((size_t)(M * 2 * I * 2)) + align256((size_t)(M * I * 2));
   if (fused) {
     SW_TRY(step_dgrad_fused(dy, W_down, preact, gp, h, M, I, Dout, st));
   } else {
     void* dout = (char*)h + align256((size_t)(M * I * 2));
+    used += align256((size_t)(M * I * 2));
     SW_TRY(step_dgrad_plain(dy, W_down, dout, M, I, Dout, st));
     SW_TRY(step_elementwise(preact, dout, gp, h, M, I, st));
   }
-  SW_TRY(step_dw_down(h, dy, dW_down, M, I, Dout, st));
-  SW_TRY(step_dx(gp, W1, dx, M, D, I, st));
-  return step_dw1(x, gp, dW1, M, D, I, st);
+  const Scratch sc{(float*)(w + used), need - used};
+  SW_TRY(step_dw_down(h, dy, dW_down, M, I, Dout, st, sc));
+  SW_TRY(step_dx(gp, W1, dx, M, D, I, st, sc));
+  return step_dw1(x, gp, dW1, M, D, I, st, sc);
 }
 
 int swiglu_mlp_bwd(const void* x, const void* W1, const void* W_down, const void* preact, const void* dy, void* dx,
@@ -713,9 +832,11 @@ int swiglu_mlp_bwd_residual(const void* x, const void* W1, const void* W_down, c
   void* gp = w;
   void* h = w + align256((size_t)(M * 2 * I * 2));
   SW_TRY(step_dgrad_fused(dy, W_down, preact, gp, h, M, I, Dout, st));
-  SW_TRY(step_dw_down(h, dy, dW_down, M, I, Dout, st));
+  const size_t used = align256((size_t)(M * 2 * I * 2)) + align256((size_t)(M * I * 2));
+  const Scratch sc{(float*)(w + used), need - used};
+  SW_TRY(step_dw_down(h, dy, dW_down, M, I, Dout, st, sc));
   SW_TRY(step_dx_residual(gp, W1, dy, dx, M, D, I, st));
-  return step_dw1(x, gp, dW1, M, D, I, st);
+  return step_dw1(x, gp, dW1, M, D, I, st, sc);
 }
 
 int swiglu_fwd_down_residual(const void* h, const void* W_down, const void* x, void* y, int64_t M, int64_t I,
@@ -827,9 +948,10 @@ int swiglu_moe_bwd_dgrad_fused(const void* dy, const void* W_down, const int32_t
 
 // --- save-h fallback (the drop-h report's normal MLPBlock) ------------------
 
+// grad_preact [M,2I] | split tail of dW_down, dx, dW1
 size_t swiglu_mlp_bwd_saved_h_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout) {
   if (check_dims(M, D, I, Dout) != SWIGLU_OK) return 0;
-  return align256((size_t)(M * 2 * I * 2));
+  return align256((size_t)(M * 2 * I * 2)) + bwd_split_bytes(M, D, I, Dout);
 }
 
 int swiglu_mlp_fwd_save_h(const void* x, const void* W1, const void* W_down, void* preact, void* h, void* y,
@@ -866,9 +988,11 @@ int swiglu_mlp_bwd_saved_h(const void* x, const void* W1, const void* W_down, co
   SW_TRY(check_alias(ins, 6, outs, 4));
   hipStream_t st = as_stream(stream);
   SW_TRY(step_dgrad_fused_gp(dy, W_down, preact, ws, M, I, Dout, st));
-  SW_TRY(step_dw_down(h, dy, dW_down, M, I, Dout, st));
-  SW_TRY(step_dx(ws, W1, dx, M, D, I, st));
-  return step_dw1(x, ws, dW1, M, D, I, st);
+  const size_t used = align256((size_t)(M * 2 * I * 2));
+  const Scratch sc{(float*)((char*)ws + used), need - used};
+  SW_TRY(step_dw_down(h, dy, dW_down, M, I, Dout, st, sc));
+  SW_TRY(step_dx(ws, W1, dx, M, D, I, st, sc));
+  return step_dw1(x, ws, dW1, M, D, I, st, sc);
 }
 
 int swiglu_bwd_dgrad_fused_gp(const void* dy, const void* W_down, const void* preact, void* grad_preact, int64_t M,

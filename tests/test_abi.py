@@ -39,9 +39,16 @@ def test_status_strings():
 def test_workspace_sizes():
     L = sw.lib()
     M, D, I, Dout = 11136, 3584, 14336, 3584
-    assert L.swiglu_mlp_fwd_workspace(M, D, I, Dout) == M * I * 2
-    assert L.swiglu_mlp_bwd_workspace(M, D, I, Dout) == M * 2 * I * 2 + M * I * 2
-    assert L.swiglu_mlp_bwd_unfused_workspace(M, D, I, Dout) == M * 2 * I * 2 + 2 * M * I * 2
+    tile = 256 * 256 * 4                       # one fp32 partial tile of the split tail
+    # 616 tiles of the down GEMM (y = h.W_down) = 2 rounds of 256 + a tail of
+    # 104, split 2 ways; the backward's largest split is dx's tail: 104 tiles, 7 parts
+    assert L.swiglu_mlp_fwd_workspace(M, D, I, Dout) == M * I * 2 + 104 * 2 * tile
+    assert L.swiglu_mlp_bwd_workspace(M, D, I, Dout) == M * 2 * I * 2 + M * I * 2 + 104 * 7 * tile
+    assert L.swiglu_mlp_bwd_unfused_workspace(M, D, I, Dout) == M * 2 * I * 2 + 2 * M * I * 2 + 104 * 7 * tile
+    assert L.swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout) == M * 2 * I * 2 + 104 * 7 * tile
+    # whole rounds of tiles (the Llama-like shape): no split tail, no extra bytes
+    assert L.swiglu_mlp_fwd_workspace(8192, 4096, 11008, 4096) == 8192 * 11008 * 2
+    assert L.swiglu_mlp_bwd_workspace(8192, 4096, 11008, 4096) == 8192 * 2 * 11008 * 2 + 8192 * 11008 * 2
     assert L.swiglu_mlp_fwd_workspace(-1, D, I, Dout) == 0
     assert L.swiglu_mlp_fwd_workspace(M, 100, I, Dout) == 0
     assert L.swiglu_mlp_bwd_workspace(0, D, I, Dout) == 0
@@ -136,7 +143,7 @@ def test_save_h_entry_points_reject_bad_arguments():
     assert fwd(*a[:4], None, a[5]) == NULL                  # h is required
     assert fwd(*a[:4], a[4] + 8, a[5]) == ALIGN
     assert fwd(*a[:4], a[3] + 64, a[5]) == ALIAS            # h inside preact
-    assert L.swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout) == M * 2 * I * 2
+    assert L.swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout) == M * 2 * I * 2   # no split tail at this size
     assert L.swiglu_mlp_bwd_saved_h_workspace(M, 100, I, Dout) == 0
     bwd = lambda p, wsb=1 << 40: L.swiglu_mlp_bwd_saved_h(*p[:9], p[9], wsb, M, D, I, Dout, None)
     p = [addr(i) for i in range(10)]

@@ -124,3 +124,26 @@ def test_decode_forward_full_oracle():
     P, _, Y = oracle.forward(*(bf16_bits_to_f64(a) for a in (xb, W1b, Wdb)))
     assert_close("preact", to_f64(pre), P)
     assert_close("y", to_f64(y), Y)
+
+
+def test_target_split_tails_match_single_launches():
+    """At the target shape the whole-step calls run the down GEMM, dW_down,
+    dx and dW1 with their last round of tiles split along K; every element
+    must be within the fp32 reordering bound of the one-launch kernels
+    (test_gpu_parity.within_reorder_bound: 1 bf16 ulp plus 2^-16 of the
+    tensor's largest magnitude)."""
+    from test_gpu_parity import within_reorder_bound
+    w = WORKLOADS["target"]
+    M, D, I, Dout = w.M, w.D, w.I, w.Dout
+    _case("split tails at", (M, D, I, Dout))
+    xb, W1b, Wdb, dyb = make_inputs(w)
+    x, W1, Wd, dy = (to_dev(a) for a in (xb, W1b, Wdb, dyb))
+    pre, y = sw.swiglu_mlp_fwd(x, W1, Wd)
+    dx, dW1, dWd = sw.swiglu_mlp_bwd(x, W1, Wd, pre, dy)
+    _, h = sw.swiglu_fwd_gemm1(x, W1)
+    y1 = sw.swiglu_fwd_down(h, Wd)
+    gp, hb = sw.swiglu_bwd_dgrad_fused(dy, Wd, pre)
+    dx1, dW11, dWd1 = sw.swiglu_bwd_dx(gp, W1), sw.swiglu_bwd_dw1(x, gp), sw.swiglu_bwd_dw_down(hb, dy)
+    torch.cuda.synchronize()
+    for name, a, b in (("y", y, y1), ("dx", dx, dx1), ("dW1", dW1, dW11), ("dW_down", dWd, dWd1)):
+        within_reorder_bound(name, a, b)

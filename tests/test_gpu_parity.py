@@ -258,6 +258,42 @@ def test_residual_step_kernels_and_autograd():
     assert np.array_equal(bits(x3.grad.reshape(-1, D)), bits(dx))
 
 
+def within_reorder_bound(name, a, b):
+    """Two GEMM results that differ only in the order of their fp32 sums (the
+    split tail adds K-parts of a tile separately): elementwise
+    |a - b| <= 1 bf16 ulp of the larger magnitude (a rounding flip) plus
+    2^-16 * max|b| (near-zero outputs, where the order changes the fp32 sum by
+    about eps32 times the partial sums' size: ~1e-6 of max|b| measured at the
+    target shape).  A missing or misplaced K-part is an O(1) error over whole
+    tiles."""
+    fa, fb = to_f64(a), to_f64(b)
+    bound = ulp_bf16(np.maximum(np.abs(fa), np.abs(fb))) + 2.0 ** -16 * np.abs(fb).max()
+    bad = np.abs(fa - fb) > bound
+    assert not bad.any(), f"{name}: {int(bad.sum())} elements beyond the reordering bound"
+
+
+@pytest.mark.parametrize("shape", [(5000, 3584, 1024, 3584), (4700, 3584, 768, 3584)])
+def test_split_tail_vs_oracle(shape):
+    """Shapes whose dx GEMM runs its last, partly filled round of tiles as a
+    split tail (K cut into parts, fp32 partial tiles, ordered reduce): the
+    whole-step calls against the full oracle, and dx within one bf16 ulp of
+    the single-launch dx kernel."""
+    M, D, I, Dout = shape
+    _case("split tail", shape)
+    _, (x, W1, Wd, dy), (xf, W1f, Wdf, dyf) = _inputs(M, D, I, Dout, seed=61)
+    pre, y = sw.swiglu_mlp_fwd(x, W1, Wd)
+    dx, dW1, dWd = sw.swiglu_mlp_bwd(x, W1, Wd, pre, dy)
+    gp, _ = sw.swiglu_bwd_dgrad_fused(dy, Wd, pre)
+    dx1 = sw.swiglu_bwd_dx(gp, W1)
+    torch.cuda.synchronize()
+    within_reorder_bound("dx split vs single launch", dx, dx1)
+    ref = oracle.backward(xf, W1f, Wdf, dyf)
+    assert_close("y", to_f64(y), ref["y"])
+    assert_close("dx", to_f64(dx), ref["dx"])
+    assert_close("dW1", to_f64(dW1), ref["dW1"])
+    assert_close("dW_down", to_f64(dWd), ref["dW_down"])
+
+
 def test_empty_batch():
     D, I, Dout = 256, 512, 256
     _case("M=0")
