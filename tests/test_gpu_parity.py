@@ -294,6 +294,33 @@ def test_split_tail_vs_oracle(shape):
     assert_close("dW_down", to_f64(dWd), ref["dW_down"])
 
 
+def _fuzz_shapes(n=24, seed=71):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 700))]))
+        D, I, Dout = (64 * int(rng.integers(1, 17)) for _ in range(3))
+        out.append((M, D, I, Dout))
+    return out
+
+
+@pytest.mark.parametrize("shape", _fuzz_shapes())
+def test_random_shapes_vs_oracle(shape):
+    """Seeded random shapes: ragged token counts from 1 to 700 (the decode
+    path at 16 rows or fewer when 2I and Dout are multiples of 128), and D, I,
+    Dout any multiples of 64 up to 1024 (every tile configuration, N tails
+    of 64)."""
+    M, D, I, Dout = shape
+    _case("fuzz", shape)
+    _, (x, W1, Wd, dy), (xf, W1f, Wdf, dyf) = _inputs(M, D, I, Dout, seed=73)
+    pre, y = sw.swiglu_mlp_fwd(x, W1, Wd)
+    dx, dW1, dWd = sw.swiglu_mlp_bwd(x, W1, Wd, pre, dy)
+    torch.cuda.synchronize()
+    ref = oracle.backward(xf, W1f, Wdf, dyf)
+    for name, got in (("preact", pre), ("y", y), ("dx", dx), ("dW1", dW1), ("dW_down", dWd)):
+        assert_close(name, to_f64(got), ref[name])
+
+
 def test_empty_batch():
     D, I, Dout = 256, 512, 256
     _case("M=0")
