@@ -147,3 +147,31 @@ def test_target_split_tails_match_single_launches():
     torch.cuda.synchronize()
     for name, a, b in (("y", y, y1), ("dx", dx, dx1), ("dW1", dW1, dW11), ("dW_down", dWd, dWd1)):
         within_reorder_bound(name, a, b)
+
+
+def test_target_residual_and_save_h_paths():
+    """The residual block and the save-h backward at the target shape, where
+    their plain-store GEMMs run split tails: the save-h backward bitwise
+    equal to the drop-h one (same kernels, same split plans), the residual
+    block's weight gradients bitwise equal to the plain block's, and its y
+    and dx on sampled rows against the oracle plus x and dy."""
+    w = WORKLOADS["target"]
+    M, D, I, Dout = w.M, w.D, w.I, w.Dout
+    _case("residual and save-h at", (M, D, I, Dout))
+    xb, W1b, Wdb, dyb = make_inputs(w)
+    x, W1, Wd, dy = (to_dev(a) for a in (xb, W1b, Wdb, dyb))
+    pre, y = sw.swiglu_mlp_fwd(x, W1, Wd)
+    dx, dW1, dWd = sw.swiglu_mlp_bwd(x, W1, Wd, pre, dy)
+    pre_s, h_s, y_s = sw.swiglu_mlp_fwd_save_h(x, W1, Wd)
+    dx_s, dW1_s, dWd_s = sw.swiglu_mlp_bwd_saved_h(x, W1, Wd, pre_s, h_s, dy)
+    pre_r, y_r = sw.swiglu_mlp_fwd_residual(x, W1, Wd)
+    dx_r, dW1_r, dWd_r = sw.swiglu_mlp_bwd_residual(x, W1, Wd, pre_r, dy)
+    torch.cuda.synchronize()
+    for a, b in ((dx_s, dx), (dW1_s, dW1), (dWd_s, dWd), (dW1_r, dW1), (dWd_r, dWd), (pre_r, pre)):
+        assert np.array_equal(bits(a), bits(b))
+    rows, chans = _sample(M, 256, 3), _sample(I, 64, 4)
+    xf, W1f, Wdf, dyf = (bf16_bits_to_f64(a) for a in (xb, W1b, Wdb, dyb))
+    s = oracle.sampled_forward_backward(xf, W1f, Wdf, dyf, rows, chans)
+    rt = torch.from_numpy(rows).cuda()
+    assert_close("residual y rows", to_f64(y_r.index_select(0, rt)), s["y_rows"] + xf[rows])
+    assert_close("residual dx rows", to_f64(dx_r.index_select(0, rt)), s["dx_rows"] + dyf[rows])
