@@ -27,10 +27,8 @@
 
 namespace swg {
 
-constexpr int SK_BN = 128;                       // columns per workgroup
+constexpr int SK_BN = 128;                       // columns per workgroup (the smaller width)
 constexpr int SK_BK = 64;                        // k rows per stage
-constexpr int SK_W_BYTES = SK_BK * SK_BN * 2;    // 16 KB of W per stage
-constexpr int SK_LDS = 2 * SK_W_BYTES;           // two stages (32 KB)
 
 struct SkinnyArgs {
   const uint16_t* X;  // [M, K] row-major
@@ -50,8 +48,17 @@ struct SkinnyArgs {
 // k-contiguous B fragments.  (For a pure stream the vector-load path reaches
 // about 7.3 TB/s on MI355X against about 6.2 TB/s for direct-to-LDS loads.)
 // The X fragments are already k-contiguous and come straight from memory.
+// BN (128 or 256) columns per workgroup: a wider block reads longer runs of
+// each W row (256 or 512 bytes), which HBM serves faster, at the cost of
+// fewer, longer streams.
+template <int BN>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(const SkinnyArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[SK_LDS];
+  constexpr int W_BYTES = SK_BK * BN * 2;   // one stage of W
+  constexpr int CPR = BN / 8;               // 16-byte chunks per W row
+  constexpr int RPP = 256 / CPR;            // W rows per load pass of the workgroup
+  constexpr int PASSES = SK_BK / RPP;       // loads per thread per stage
+  constexpr int NT = BN / 64;               // 16-column MFMA tiles per wave
+  __shared__ __attribute__((aligned(1024))) char smem[2 * W_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = blockIdx.x, s = blockIdx.y;
@@ -59,23 +66,23 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const SkinnyArgs a) {
   const int kt0 = s * a.stages_per_split;
   const int nk = min(a.stages_per_split, nk_all - kt0);  // >= 1 by the host's choice of S
 
-  // W: thread t moves chunk c = t%16 (8 columns) of k-rows t/16 + 16i, i < 4;
-  // one wave instruction covers four 256-byte row segments
-  const int wc = tid & 15, wr = tid >> 4;
-  const uint16_t* wsrc = a.W + ((int64_t)kt0 * SK_BK + wr) * a.ldw + (int64_t)nb * SK_BN + wc * 8;
-  int woff[4];
+  // W: thread t moves chunk c = t%CPR (8 columns) of k-rows t/CPR + RPP*i;
+  // one wave instruction covers BN*2-byte segments of 64/CPR rows
+  const int wc = tid % CPR, wr = tid / CPR;
+  const uint16_t* wsrc = a.W + ((int64_t)kt0 * SK_BK + wr) * a.ldw + (int64_t)nb * BN + wc * 8;
+  int woff[PASSES];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) woff[i] = lds_off_mn<SK_BN>(wr + 16 * i, wc);
+  for (int i = 0; i < PASSES; ++i) woff[i] = lds_off_mn<BN>(wr + RPP * i, wc);
   // X: lane l holds row l%16, k-octet (kk*4 + l/16) of the stage.  Rows
   // >= M repeat row M-1: they only feed partial-sum rows >= M, which the
   // reduction never reads.
   const int xr = lane & 15, xo = lane >> 4;
   const uint16_t* xsrc = a.X + (int64_t)min(xr, a.M - 1) * a.ldx + (int64_t)kt0 * SK_BK + xo * 8;
 
-  auto load_w = [&](int j, u32x4 (&r)[4]) {
+  auto load_w = [&](int j, u32x4 (&r)[PASSES]) {
     const uint16_t* p = wsrc + (int64_t)j * SK_BK * a.ldw;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = __builtin_nontemporal_load((const u32x4*)(p + (int64_t)16 * i * a.ldw));
+    for (int i = 0; i < PASSES; ++i) r[i] = __builtin_nontemporal_load((const u32x4*)(p + (int64_t)RPP * i * a.ldw));
   };
   auto load_x = [&](int j, bf16x8 (&r)[2]) {
 #pragma unroll
@@ -85,17 +92,19 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const SkinnyArgs a) {
   };
 
   typedef float f32x4v __attribute__((ext_vector_type(4)));
-  f32x4v acc[2] = {f32x4v{}, f32x4v{}};  // this wave's two 16-column tiles
-  u32x4 wreg[2][4];
+  f32x4v acc[NT];  // this wave's 16-column tiles
+#pragma unroll
+  for (int u = 0; u < NT; ++u) acc[u] = f32x4v{};
+  u32x4 wreg[2][PASSES];
   bf16x8 xreg[2][2];
 
   auto stage = [&](int kt, int b, bool refill) {
     // stage kt's W registers -> LDS buffer b; refill them with stage kt+2.
     // Stage kt+2's X is loaded after this stage's MFMAs have used stage kt's,
     // so no register holding a pending load is ever copied.
-    SWG_LDS char* t = (SWG_LDS char*)smem + b * SK_W_BYTES;
+    SWG_LDS char* t = (SWG_LDS char*)smem + b * W_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(SWG_LDS u32x4*)(t + woff[i]) = wreg[b][i];
+    for (int i = 0; i < PASSES; ++i) *(SWG_LDS u32x4*)(t + woff[i]) = wreg[b][i];
     if (refill) load_w(kt + 2, wreg[b]);
     // every wave's part of stage kt is in LDS; buffer b's previous readers
     // (stage kt-2) finished before the barrier of stage kt-1
@@ -109,10 +118,10 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const SkinnyArgs a) {
       const int g = lane >> 4, j = lane & 15, e = j >> 2, q = j & 3;
       const int kbase = kk * 32 + g * 8 + e;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int col = (wave * 2 + u) * 16 + q * 4;
-        const int o1 = lds_off_mn<SK_BN>(kbase, col >> 3) + (col & 7) * 2;
-        const int o2 = lds_off_mn<SK_BN>(kbase + 4, col >> 3) + (col & 7) * 2;
+      for (int u = 0; u < NT; ++u) {
+        const int col = (wave * NT + u) * 16 + q * 4;
+        const int o1 = lds_off_mn<BN>(kbase, col >> 3) + (col & 7) * 2;
+        const int o2 = lds_off_mn<BN>(kbase + 4, col >> 3) + (col & 7) * 2;
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWG_LDS i16x4*)(t + o1));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWG_LDS i16x4*)(t + o2));
         const bf16x8 wb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -141,10 +150,10 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const SkinnyArgs a) {
   if (rest >= 2) stage(kt + 1, 1, false);
   if (rest >= 3) stage(kt + 2, 0, false);
   // D of 16x16x32: lane l holds column l%16, rows 4*(l/16) .. +3
-  float* out = a.partial + (int64_t)s * 16 * a.N + (int64_t)nb * SK_BN;
+  float* out = a.partial + (int64_t)s * 16 * a.N + (int64_t)nb * BN;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int col = (wave * 2 + u) * 16 + (lane & 15);
+  for (int u = 0; u < NT; ++u) {
+    const int col = (wave * NT + u) * 16 + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[(int64_t)(4 * (lane >> 4) + i) * a.N + col] = acc[u][i];
   }

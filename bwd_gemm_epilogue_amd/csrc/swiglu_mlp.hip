@@ -407,12 +407,12 @@ int run_store_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
 // workgroups (K is a multiple of 64 for every GEMM here).
 bool skinny_fits(int64_t M, int64_t N) { return M >= 1 && M <= 16 && N % SK_BN == 0; }
 
-// Split-K factor: about 512 workgroups (two per CU of MI355X; more splits
-// measured slower: more partial-sum traffic and shorter streams per
-// workgroup) with every split non-empty.  stages_per_split is returned
-// through *spp.
-int skinny_splits(int64_t N, int64_t K, int* spp) {
-  const int64_t nblk = N / SK_BN, nk = K / SK_BK;
+// Split-K factor for BN-wide column blocks: about 512 workgroups (two per CU
+// of MI355X; more splits measured slower: more partial-sum traffic and
+// shorter streams per workgroup) with every split non-empty.
+// stages_per_split is returned through *spp.
+int skinny_splits(int64_t N, int64_t K, int bn, int* spp) {
+  const int64_t nblk = N / bn, nk = K / SK_BK;
   int64_t S = 512 / nblk;
   if (S < 1) S = 1;
   if (S > nk) S = nk;
@@ -421,16 +421,21 @@ int skinny_splits(int64_t N, int64_t K, int* spp) {
   return (int)((nk + per - 1) / per);
 }
 
+// Column-block width: 256 (512-byte runs of each W row) for GEMM-1's wide
+// [D, 2I] when it divides; 128 otherwise (the down GEMM's narrower W would
+// get too few, too short streams at 256).
+int skinny_bn_gemm1(int64_t I) { return (2 * I) % 256 == 0 ? 256 : SK_BN; }
+
 bool fwd_is_skinny(int64_t M, int64_t I, int64_t Dout) { return skinny_fits(M, 2 * I) && skinny_fits(M, Dout); }
 
 size_t skinny_partial_bytes(int64_t D, int64_t I, int64_t Dout) {
   int spp;
-  const size_t a = (size_t)skinny_splits(2 * I, D, &spp) * 16 * (size_t)(2 * I) * 4;
-  const size_t b = (size_t)skinny_splits(Dout, I, &spp) * 16 * (size_t)Dout * 4;
+  const size_t a = (size_t)skinny_splits(2 * I, D, skinny_bn_gemm1(I), &spp) * 16 * (size_t)(2 * I) * 4;
+  const size_t b = (size_t)skinny_splits(Dout, I, SK_BN, &spp) * 16 * (size_t)Dout * 4;
   return a > b ? a : b;
 }
 
-int run_skinny(const void* X, int64_t ldx, const void* W, int64_t M, int64_t N, int64_t K, float* partial,
+int run_skinny(const void* X, int64_t ldx, const void* W, int64_t M, int64_t N, int64_t K, int bn, float* partial,
                hipStream_t st, int* S_out) {
   SkinnyArgs a;
   a.X = (const uint16_t*)X;
@@ -441,9 +446,12 @@ int run_skinny(const void* X, int64_t ldx, const void* W, int64_t M, int64_t N, 
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
-  const int S = skinny_splits(N, K, &a.stages_per_split);
+  const int S = skinny_splits(N, K, bn, &a.stages_per_split);
   *S_out = S;
-  hipLaunchKernelGGL(skinny_gemm_kernel, dim3((unsigned)(N / SK_BN), (unsigned)S), dim3(256), 0, st, a);
+  if (bn == 256)
+    hipLaunchKernelGGL(skinny_gemm_kernel<256>, dim3((unsigned)(N / 256), (unsigned)S), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(skinny_gemm_kernel<SK_BN>, dim3((unsigned)(N / SK_BN), (unsigned)S), dim3(256), 0, st, a);
   return launch_status();
 }
 
@@ -451,12 +459,12 @@ int run_skinny(const void* X, int64_t ldx, const void* W, int64_t M, int64_t N, 
 int fwd_skinny(const void* x, const void* W1, const void* Wd, void* preact, void* y, void* h, float* partial,
                int64_t M, int64_t D, int64_t I, int64_t Dout, hipStream_t st, const void* residual = nullptr) {
   int S;
-  SW_TRY(run_skinny(x, D, W1, M, 2 * I, D, partial, st, &S));
+  SW_TRY(run_skinny(x, D, W1, M, 2 * I, D, skinny_bn_gemm1(I), partial, st, &S));
   const int64_t t1 = M * (I / 8);
   hipLaunchKernelGGL(skinny_swiglu_reduce_kernel, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, st, partial, S,
                      (int)M, I, (uint16_t*)preact, (uint16_t*)h);
   SW_TRY(launch_status());
-  SW_TRY(run_skinny(h, I, Wd, M, Dout, I, partial, st, &S));
+  SW_TRY(run_skinny(h, I, Wd, M, Dout, I, SK_BN, partial, st, &S));
   const int64_t t2 = M * (Dout / 8);
   hipLaunchKernelGGL(skinny_store_reduce_kernel, dim3((unsigned)((t2 + 255) / 256)), dim3(256), 0, st, partial, S,
                      (int)M, Dout, (uint16_t*)y, (const uint16_t*)residual);
