@@ -145,6 +145,31 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
   return r;
 }
 
+// Epilogue accesses are buffer instructions on a descriptor that starts at
+// the tile's first row and ends at the row bound: rows at or past it fall
+// outside num_records, so their loads return zeros and their stores are
+// dropped by the hardware range check.  The epilogue then has no branch
+// around a global access.  (Under `if (row < M)` branches the compiler's
+// wait-count pass lost count of the prefetched loads and waited for every
+// outstanding access, vmcnt(0), before each 8-column chunk, which undid the
+// prefetch.)  Offsets are 32-bit bytes from the tile's first row: a tile
+// spans at most 256 rows of at most 2^21 elements.
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
+__device__ __forceinline__ brsrc_t rows_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0ll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
+}
+// an offset past every num_records above: the access is dropped
+constexpr uint32_t kOffOutOfRange = 0x80000000u;
+// cache policy of the epilogue's accesses: nontemporal (streamed once)
+constexpr int kPolicyNT = 2;
+__device__ __forceinline__ u32x4 bload16(brsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicyNT);
+}
+__device__ __forceinline__ void bstore16(brsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolicyNT);
+}
+
 // One wave-wide direct-to-LDS load: lane i's 16 B at byte offset
 // vbase + sadd of the buffer land at LDS address dst + 16*i.  Issued as
 // inline asm so that the compiler's wait-count pass does not track these LDS
@@ -652,15 +677,15 @@ struct EpiStore {
     constexpr int CPR = T::BN / 8;  // 8-column chunks per slab row
     constexpr int ITEMS = T::SLAB_ROWS * CPR;
     static_assert(ITEMS % T::THREADS == 0, "slab items must split evenly");
+    const brsrc_t dst = rows_rsrc(p.C + c.goff + (int64_t)c.r0 * p.ldc, (int64_t)(c.M - c.r0) * p.ldc * 2);
+    const int ldc = (int)p.ldc;
 #pragma unroll
     for (int k = 0; k < ITEMS / T::THREADS; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
-      const int row = c.row(sr), col = c.tn * T::BN + ch * 8;
-      if (row < c.M && col < c.N) {
-        u32x4 v = pack8(c.read8(sr, ch * 8));
-        *(u32x4*)(p.C + c.goff + (int64_t)row * p.ldc + col) = v;
-      }
+      const int col = c.tn * T::BN + ch * 8;
+      const uint32_t off = col < c.N ? (uint32_t)((c.row(sr) - c.r0) * ldc + col) * 2u : kOffOutOfRange;
+      bstore16(dst, off, pack8(c.read8(sr, ch * 8)));
     }
   }
 };
@@ -749,29 +774,33 @@ struct EpiStoreResidual {
   template <class T>
   __device__ static void prefetch(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
     constexpr int CPR = T::BN / 8;
+    const brsrc_t src = rows_rsrc(p.R + (int64_t)c.r0 * p.ldr, (int64_t)(c.M - c.r0) * p.ldr * 2);
+    const int ldr = (int)p.ldr;
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
-      const int row = c.row(sr), col = c.tn * T::BN + ch * 8;
-      if (row < c.M && col < c.N) pf.r[k] = __builtin_nontemporal_load((const u32x4*)(p.R + (int64_t)row * p.ldr + col));
+      const int col = c.tn * T::BN + ch * 8;
+      const uint32_t off = col < c.N ? (uint32_t)((c.row(sr) - c.r0) * ldr + col) * 2u : kOffOutOfRange;
+      pf.r[k] = bload16(src, off);
     }
   }
   template <class T>
   __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
     constexpr int CPR = T::BN / 8;
+    const brsrc_t dst = rows_rsrc(p.C + (int64_t)c.r0 * p.ldc, (int64_t)(c.M - c.r0) * p.ldc * 2);
+    const int ldc = (int)p.ldc;
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
-      const int row = c.row(sr), col = c.tn * T::BN + ch * 8;
-      if (row < c.M && col < c.N) {
-        f32x8 v = c.read8(sr, ch * 8);
-        const f32x8 r = unpack8(pf.r[k]);
+      const int col = c.tn * T::BN + ch * 8;
+      const uint32_t off = col < c.N ? (uint32_t)((c.row(sr) - c.r0) * ldc + col) * 2u : kOffOutOfRange;
+      f32x8 v = c.read8(sr, ch * 8);
+      const f32x8 r = unpack8(pf.r[k]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += r[e];
-        *(u32x4*)(p.C + (int64_t)row * p.ldc + col) = pack8(v);
-      }
+      for (int e = 0; e < 8; ++e) v[e] += r[e];
+      bstore16(dst, off, pack8(v));
     }
   }
 };

@@ -46,25 +46,27 @@ struct EpiSwigluFwd {
     constexpr int CPR = HALF / 8;
     constexpr int ITEMS = T::SLAB_ROWS * CPR;
     static_assert(ITEMS % T::THREADS == 0, "slab items must split evenly");
+    const int I = (int)p.I;
+    const int64_t rows = c.M - c.r0;
+    const brsrc_t pdst = rows_rsrc(p.preact + (int64_t)c.r0 * 2 * p.I, rows * 4 * p.I);
+    const brsrc_t hdst = rows_rsrc(p.h + (int64_t)c.r0 * p.I, rows * 2 * p.I);
 #pragma unroll
     for (int k = 0; k < ITEMS / T::THREADS; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
-      const int row = c.row(sr);
-      const int64_t i0 = (int64_t)c.tn * HALF + ch * 8;
-      if (row < c.M) {
-        const u32x4 lp = pack8(c.read8(sr, ch * 8));
-        const u32x4 gp = pack8(c.read8(sr, HALF + ch * 8));
-        const f32x8 left = unpack8(lp), gate = unpack8(gp);
-        f32x8 h;
+      const int rl = c.row(sr) - c.r0;
+      const int i0 = c.tn * HALF + ch * 8;
+      const u32x4 lp = pack8(c.read8(sr, ch * 8));
+      const u32x4 gp = pack8(c.read8(sr, HALF + ch * 8));
+      const f32x8 left = unpack8(lp), gate = unpack8(gp);
+      f32x8 h;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = swiglu_h(left[e], gate[e]);
-        uint16_t* pr = p.preact + (int64_t)row * 2 * p.I;
-        // streaming stores: nothing in this kernel reads them back
-        __builtin_nontemporal_store(lp, (u32x4*)(pr + i0));
-        __builtin_nontemporal_store(gp, (u32x4*)(pr + p.I + i0));
-        __builtin_nontemporal_store(pack8(h), (u32x4*)(p.h + (int64_t)row * p.I + i0));
-      }
+      for (int e = 0; e < 8; ++e) h[e] = swiglu_h(left[e], gate[e]);
+      // streaming stores: nothing in this kernel reads them back
+      const uint32_t off = (uint32_t)(rl * 2 * I + i0) * 2u;
+      bstore16(pdst, off, lp);
+      bstore16(pdst, off + (uint32_t)I * 2u, gp);
+      bstore16(hdst, (uint32_t)(rl * I + i0) * 2u, pack8(h));
     }
   }
 };
@@ -104,51 +106,45 @@ struct EpiSwigluBwdT {
   __device__ static void prefetch(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
     constexpr int CPR = T::BN / 8;
     const int I = (int)p.I;
-    const char* base = (const char*)(p.preact + (int64_t)c.r0 * 2 * p.I);
+    const brsrc_t src = rows_rsrc(p.preact + (int64_t)c.r0 * 2 * p.I, (int64_t)(c.M - c.r0) * 4 * p.I);
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
-      const int row = c.row(sr);
-      const int rl = row - c.r0;
+      const int rl = c.row(sr) - c.r0;
       const uint32_t off = (uint32_t)(rl * 2 * I + c.tn * T::BN + ch * 8) * 2u;
-      if (row < c.M) {
-        pf.left[k] = __builtin_nontemporal_load((const u32x4*)(base + off));
-        pf.gate[k] = __builtin_nontemporal_load((const u32x4*)(base + off + (uint32_t)I * 2u));
-      }
+      pf.left[k] = bload16(src, off);
+      pf.gate[k] = bload16(src, off + (uint32_t)I * 2u);
     }
   }
   template <class T>
   __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
     constexpr int CPR = T::BN / 8;
     const int I = (int)p.I;
-    char* gbase = (char*)(p.grad_preact + (int64_t)c.r0 * 2 * p.I);
-    char* hbase = STORE_H ? (char*)(p.h + (int64_t)c.r0 * p.I) : nullptr;
+    const int64_t rows = c.M - c.r0;
+    const brsrc_t gdst = rows_rsrc(p.grad_preact + (int64_t)c.r0 * 2 * p.I, rows * 4 * p.I);
+    const brsrc_t hdst = rows_rsrc(STORE_H ? p.h + (int64_t)c.r0 * p.I : nullptr, STORE_H ? rows * 2 * p.I : 0);
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
-      const int row = c.row(sr);
-      const int rl = row - c.r0;
+      const int rl = c.row(sr) - c.r0;
       const int col = c.tn * T::BN + ch * 8;
-      if (row < c.M) {
-        const f32x8 dout = c.read8(sr, ch * 8);
-        const f32x8 left = unpack8(pf.left[k]), gate = unpack8(pf.gate[k]);
-        f32x8 dl, dg, h;
+      const f32x8 dout = c.read8(sr, ch * 8);
+      const f32x8 left = unpack8(pf.left[k]), gate = unpack8(pf.gate[k]);
+      f32x8 dl, dg, h;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const Act a = sw_act(gate[e]);
-          dl[e] = dout[e] * a.silu;
-          dg[e] = (dout[e] * left[e]) * a.dsilu;
-          h[e] = left[e] * a.silu;
-        }
-        const uint32_t off = (uint32_t)(rl * 2 * I + col) * 2u;
-        const uint32_t offh = (uint32_t)(rl * I + col) * 2u;
-        // streaming stores: nothing in this kernel reads them back
-        __builtin_nontemporal_store(pack8(dl), (u32x4*)(gbase + off));
-        __builtin_nontemporal_store(pack8(dg), (u32x4*)(gbase + off + (uint32_t)I * 2u));
-        if constexpr (STORE_H) __builtin_nontemporal_store(pack8(h), (u32x4*)(hbase + offh));
+      for (int e = 0; e < 8; ++e) {
+        const Act a = sw_act(gate[e]);
+        dl[e] = dout[e] * a.silu;
+        dg[e] = (dout[e] * left[e]) * a.dsilu;
+        h[e] = left[e] * a.silu;
       }
+      const uint32_t off = (uint32_t)(rl * 2 * I + col) * 2u;
+      // streaming stores: nothing in this kernel reads them back
+      bstore16(gdst, off, pack8(dl));
+      bstore16(gdst, off + (uint32_t)I * 2u, pack8(dg));
+      if constexpr (STORE_H) bstore16(hdst, (uint32_t)(rl * I + col) * 2u, pack8(h));
     }
   }
 };
