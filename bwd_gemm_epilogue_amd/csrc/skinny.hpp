@@ -131,12 +131,16 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const SkinnyArgs a) {
     if (refill) load_x(kt + 2, xreg[b]);
   };
 
+  // Both prologue stages are loaded unconditionally and in stage order
+  // (stage 0 twice when the split has a single stage), so that the loop is
+  // entered with the same loads pending as on every later trip.  Under an
+  // `if (nk > 1)` the compiler had issued stage 1 first, and the wait-count
+  // pass, which merges the entry and back-edge states, then made every trip
+  // wait for the stage loaded one stage earlier instead of two.
   load_w(0, wreg[0]);
   load_x(0, xreg[0]);
-  if (nk > 1) {
-    load_w(1, wreg[1]);
-    load_x(1, xreg[1]);
-  }
+  load_w(nk > 1 ? 1 : 0, wreg[1]);
+  load_x(nk > 1 ? 1 : 0, xreg[1]);
   // Steady state with unconditional refills, so that the compiler's
   // wait-count tracking sees the same loads pending on every trip (stage
   // kt+1's) and waits only for stage kt's; then the last one to three stages.
