@@ -403,13 +403,15 @@ int run_store_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
 // workgroups (K is a multiple of 64 for every GEMM here).
 bool skinny_fits(int64_t M, int64_t N) { return M >= 1 && M <= 16 && N % SK_BN == 0; }
 
-// Split-K factor for BN-wide column blocks: about 512 workgroups (two per CU
-// of MI355X; more splits measured slower: more partial-sum traffic and
-// shorter streams per workgroup) with every split non-empty.
+// Split-K factor for BN-wide column blocks: at most one workgroup per CU,
+// with every split non-empty.  At 16 x 4096 x 14336 one workgroup per CU
+// (GEMM-1: 2 splits of 112 blocks, the down GEMM: 8 of 32) measured 66 us
+// per forward against 71 us at two per CU and 72-79 us at three or four:
+// longer streams per workgroup and fewer partial sums to add.
 // stages_per_split is returned through *spp.
 int skinny_splits(int64_t N, int64_t K, int bn, int* spp) {
   const int64_t nblk = N / bn, nk = K / SK_BK;
-  int64_t S = 512 / nblk;
+  int64_t S = kComputeUnits / nblk;
   if (S < 1) S = 1;
   if (S > nk) S = nk;
   const int64_t per = (nk + S - 1) / S;
