@@ -119,13 +119,27 @@ __device__ __forceinline__ int swz_k(int r) {
 template <int BK>
 __device__ __forceinline__ int lds_off_k(int r, int c) { return r * (BK * 2) + ((c ^ swz_k<BK>(r)) << 4); }
 
-// MN-major tile [BK][ROWS]: k-rows of ROWS/8 chunks.  The chunk index is
-// XOR-ed with 2*(k%4) so that the four k-rows one ds_read_b64_tr_b16 group
-// reads land 32 B apart in the banks.  The XOR stays inside a 128 B line.
-__device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 1; }
+// MN-major tile [BK][ROWS]: k-rows of ROWS/8 chunks.  One
+// ds_read_b64_tr_b16 reads a 64 B run (4 chunks) from each of four
+// consecutive k-rows (and again from the four 8 rows further on).  The
+// chunk index is XOR-ed with a function of k%4 so that those four runs fall
+// in four different 64 B quarters of the 64 banks (256 B):
+//   ROWS >= 128 (k-rows of 256 or 512 B, all starting at bank 0): XOR
+//     4*(k%4), which moves the run to quarter (q ^ k%4) of its 256 B;
+//   ROWS = 64 (k-rows of 128 B: odd rows start at bank 32): XOR 2*(k%4),
+//     which moves rows k%4 >= 2 to the other 64 B of their half.
+// (2*(k%4) for the wider rows left rows k and k+1 in the same quarter: a
+// two-way bank conflict, measured at 12-15% of all cycles of the GEMMs with
+// two MN-major operands.)  The XOR stays below ROWS/8: it permutes the
+// chunks of one k-row.
+template <int ROWS>
+__device__ __forceinline__ int swz_mn(int k) {
+  if constexpr (ROWS >= 128) return (k & 3) << 2;
+  else return (k & 3) << 1;
+}
 template <int ROWS>
 __device__ __forceinline__ int lds_off_mn(int k, int c) {
-  return k * (ROWS * 2) + ((c ^ swz_mn(k)) << 4);
+  return k * (ROWS * 2) + ((c ^ swz_mn<ROWS>(k)) << 4);
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -217,9 +231,9 @@ __device__ __forceinline__ int mn_col(int c, int tile, int pair_off) {
 //            rows 8b .. 8b+7, row 8b + lane/8 gets chunk (lane%8) ^ swz, and
 //            swz = (lane/8) ^ (b%8): class b%8, uniform part 16*b*ld + 2*k0.
 //   MN-major: rsrc is based at k-row k0 of the operand; block b holds k-rows
-//            KROWS*b .. with KROWS = 512/ROWS, and the swizzle of k-row k is
-//            2*(k%4): class b%2 when KROWS = 2, none otherwise; uniform part
-//            2*KROWS*b*ld.
+//            KROWS*b .. with KROWS = 512/ROWS, and the swizzle of k-row k
+//            depends on k%4 only: class b%2 when KROWS = 2, none otherwise;
+//            uniform part 2*KROWS*b*ld.
 template <int ROWS, bool KMAJ>
 __device__ __forceinline__ uint32_t dma_lane_base(int64_t ld, int tile, int pair_off, int b, int lane) {
   if constexpr (KMAJ) {
@@ -230,7 +244,7 @@ __device__ __forceinline__ uint32_t dma_lane_base(int64_t ld, int tile, int pair
     constexpr int CPR = ROWS / 8, KROWS = 64 / CPR;
     const int kr = lane / CPR;
     const int k = KROWS * b + kr;
-    const int c = (lane % CPR) ^ swz_mn(k);
+    const int c = (lane % CPR) ^ swz_mn<ROWS>(k);
     const int col = mn_col<ROWS>(c * 8, tile, pair_off);
     return (uint32_t)(kr * ld * 2) + (uint32_t)col * 2u;
   }
