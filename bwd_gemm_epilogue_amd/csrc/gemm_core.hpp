@@ -144,6 +144,12 @@ __device__ __forceinline__ int lds_off_mn(int k, int c) {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// compile-time bool carried by a type (selects a variant of a generic lambda)
+template <bool V>
+struct integral_c {
+  static constexpr bool value = V;
+};
+
 // Buffer descriptor (V#) of a raw byte range: 48-bit base, stride 0,
 // num_records = bytes, dword 3 = 0x00020000 (32-bit data format, as gfx9
 // expects for untyped access).  The range check zero-fills any 16 B load at
@@ -192,8 +198,9 @@ __device__ __forceinline__ void bstore16(brsrc_t r, uint32_t off, u32x4 v) {
 // (wait_vmcnt + barrier in the main loop).  The offset is summed inside the
 // asm so that the compiler keeps one per-lane base per swizzle class instead
 // of hoisting one VGPR per 1 KB block out of the K loop.  M0 holds the LDS
-// base; the s_nop is the one wait state the hardware needs between writing
-// M0 and an LDS DMA reading it.  M0 is a reserved register: the compiler keeps
+// base; the v_add between writing M0 and the LDS DMA that reads it is the
+// one wait state the hardware needs there (an s_nop before cost one more
+// issue slot per load).  M0 is a reserved register: the compiler keeps
 // no value in it across this code (it sets it right before the few
 // instructions that read it, none of which these kernels use), so it is not
 // restored.
@@ -201,9 +208,8 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, SWG_LDS char* dst, uint
   const int m0 = __builtin_amdgcn_readfirstlane((int)(uintptr_t)dst);
   uint32_t voff;
   asm volatile(
-      "v_add_u32 %0, %1, %2\n\t"
       "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
+      "v_add_u32 %0, %1, %2\n\t"
       "buffer_load_dwordx4 %0, %4, 0 offen lds"
       : "=&v"(voff)
       : "v"(vbase), "s"(sadd), "s"(m0), "s"(rsrc)
@@ -606,39 +612,52 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
     barrier();
     load_frags<T, A_K, B_K>(a_ptr(0), b_ptr(0), f[0], 0, wm, wn, lane);
   }
-  for (int kt = 0; kt < nk; ++kt) {
+  // One stage of the K loop.  LDA / LDB: whether it issues A(kt+2) /
+  // B(kt+2).  The three variants are chosen once per stage, so the loads
+  // themselves sit in straight-line code between the MFMAs (a branch around
+  // each of them had cost issue slots the MFMA pipe waited on).
+  auto stage = [&](int kt, auto lda, auto ldb) {
+    constexpr bool LDA = decltype(lda)::value, LDB = decltype(ldb)::value;
     const SWG_LDS char* as = a_ptr(kt);
     const SWG_LDS char* bs = b_ptr(kt);
+    // LDB holds exactly when kt + 2 < nk: then this is not one of the last
+    // two stages
+    const bool last = LDB ? false : kt + 1 == nk;
+    const bool next = LDB ? true : kt + 1 < nk;
     // the epilogue's first global reads go out under the last stage's MFMAs
-    if (kt + 1 == nk) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, r0, tn, 0, m_end, g.N, goff}, pf[0], tid);
+    if (last) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, r0, tn, 0, m_end, g.N, goff}, pf[0], tid);
     // steps 0 and 1: A(kt+2), half in each (A(2) came with the prologue)
-    const bool load_a_now = kt >= 1 && kt + 2 < nk;
     const i32x4 rA = rs_a(kt + 2);
-    step<T, A_K, B_K, LA / 2>(as, bs, f[0], f[1], 1, acc, wm, wn, lane, [&](int i) {
-      if (load_a_now) load_a(rA, kt + 2, i);
+    step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[0], f[1], 1, acc, wm, wn, lane, [&](int i) {
+      if constexpr (LDA) load_a(rA, kt + 2, i);
     });
-    step<T, A_K, B_K, LA / 2>(as, bs, f[1], f[0], 2, acc, wm, wn, lane, [&](int i) {
-      if (load_a_now) load_a(rA, kt + 2, LA / 2 + i);
+    step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[1], f[0], 2, acc, wm, wn, lane, [&](int i) {
+      if constexpr (LDA) load_a(rA, kt + 2, LA / 2 + i);
     });
     step<T, A_K, B_K, 0>(as, bs, f[0], f[1], 3, acc, wm, wn, lane, no_load);
     // step 3: barrier, then the next stage's first fragments and B(kt+2)
     const SWG_LDS char* nas = as;
     const SWG_LDS char* nbs = bs;
-    if (kt + 1 < nk) {
+    if (next) {
       // A(kt+1) and B(kt+1) must have landed; A(kt+2), issued after them,
       // may stay in flight
-      if (kt + 2 < nk) wait_vmcnt<LA>();
+      if (LDB) wait_vmcnt<LA>();
       else wait_vmcnt<0>();
       barrier();
       nas = a_ptr(kt + 1);
       nbs = b_ptr(kt + 1);
     }
-    const bool load_b_now = kt + 2 < nk;
     const i32x4 rB = rs_b(kt + 2);
-    step<T, A_K, B_K, LB>(nas, nbs, f[1], f[0], 0, acc, wm, wn, lane, [&](int i) {
-      if (load_b_now) load_b(rB, kt + 2, i);
+    step<T, A_K, B_K, LDB ? LB : 0>(nas, nbs, f[1], f[0], 0, acc, wm, wn, lane, [&](int i) {
+      if constexpr (LDB) load_b(rB, kt + 2, i);
     });
-  }
+  };
+  typedef integral_c<true> yes;
+  typedef integral_c<false> no;
+  int kt = 0;
+  if (nk > 2) stage(kt++, no{}, yes{});         // stage 0: A(2) came with the prologue
+  for (; kt + 2 < nk; ++kt) stage(kt, yes{}, yes{});
+  for (; kt < nk; ++kt) stage(kt, no{}, no{});  // the last two stages load nothing
   // Every stage load has been waited for.  The only vector memory reads in
   // flight now are the epilogue prefetches, which must stay in flight: the
   // barriers below are bare s_barriers, not __syncthreads() (whose fence
