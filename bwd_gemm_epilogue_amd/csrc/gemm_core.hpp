@@ -149,6 +149,12 @@ template <bool V>
 struct integral_c {
   static constexpr bool value = V;
 };
+// compile-time int carried by a type; converts to int
+template <int V>
+struct int_c {
+  static constexpr int value = V;
+  __device__ constexpr operator int() const { return V; }
+};
 
 // Buffer descriptor (V#) of a raw byte range: 48-bit base, stride 0,
 // num_records = bytes, dword 3 = 0x00020000 (32-bit data format, as gfx9
@@ -548,8 +554,11 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   static_assert(KS == 4, "A loads use steps 0 and 1, B loads step 3");
   constexpr int LA = T::LA, LB = T::LB;
   static_assert(LA % 2 == 0, "A loads split over two steps");
-  auto a_ptr = [&](int j) { return (SWG_LDS char*)smem + (j % 3) * T::A_BYTES; };
-  auto b_ptr = [&](int j) { return (SWG_LDS char*)smem + 3 * T::A_BYTES + (j & 1) * T::B_BYTES; };
+  // ring slots: A(j) in A buffer j % 3, B(j) in B buffer j % 2
+  auto a_buf = [&](int s) { return (SWG_LDS char*)smem + s * T::A_BYTES; };
+  auto b_buf = [&](int s) { return (SWG_LDS char*)smem + 3 * T::A_BYTES + s * T::B_BYTES; };
+  auto a_ptr = [&](int j) { return a_buf(j % 3); };
+  auto b_ptr = [&](int j) { return b_buf(j & 1); };
   // descriptors: K-major fixed, MN-major rebased at the stage's first k-row
   auto rs_a = [&](int j) -> i32x4 {
     if constexpr (A_K) return ra;
@@ -567,14 +576,17 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   const uint32_t va1 = dma_lane_base<T::BM, A_K>(g.lda, tm, 0, wave + T::WAVES, lane);
   const uint32_t vb0 = dma_lane_base<T::BN, B_K>(g.ldb, tn, g.pair_off, wave, lane);
   const uint32_t vb1 = dma_lane_base<T::BN, B_K>(g.ldb, tn, g.pair_off, wave + T::WAVES, lane);
-  auto load_a = [&](const i32x4& r, int j, int idx) {
+  // load block idx of stage j into ring slot s (s = j % 3 for A, j % 2 for B)
+  auto load_a_to = [&](const i32x4& r, int j, int s, int idx) {
     const int b = wave + idx * T::WAVES;
-    dma16(r, a_ptr(j) + b * 1024, (idx & 1) ? va1 : va0, dma_block_add<T::BM, A_K>(g.lda, b, A_K ? j * T::BK : 0));
+    dma16(r, a_buf(s) + b * 1024, (idx & 1) ? va1 : va0, dma_block_add<T::BM, A_K>(g.lda, b, A_K ? j * T::BK : 0));
   };
-  auto load_b = [&](const i32x4& r, int j, int idx) {
+  auto load_b_to = [&](const i32x4& r, int j, int s, int idx) {
     const int b = wave + idx * T::WAVES;
-    dma16(r, b_ptr(j) + b * 1024, (idx & 1) ? vb1 : vb0, dma_block_add<T::BN, B_K>(g.ldb, b, B_K ? j * T::BK : 0));
+    dma16(r, b_buf(s) + b * 1024, (idx & 1) ? vb1 : vb0, dma_block_add<T::BN, B_K>(g.ldb, b, B_K ? j * T::BK : 0));
   };
+  auto load_a = [&](const i32x4& r, int j, int idx) { load_a_to(r, j, j % 3, idx); };
+  auto load_b = [&](const i32x4& r, int j, int idx) { load_b_to(r, j, j & 1, idx); };
   // A bare s_barrier after an explicit lgkmcnt(0): __syncthreads() would add
   // a release fence that drains every outstanding LDS DMA (vmcnt(0)) and
   // serialises the ring.  The clobber keeps the compiler from moving LDS
@@ -615,11 +627,17 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   // One stage of the K loop.  LDA / LDB: whether it issues A(kt+2) /
   // B(kt+2).  The three variants are chosen once per stage, so the loads
   // themselves sit in straight-line code between the MFMAs (a branch around
-  // each of them had cost issue slots the MFMA pipe waited on).
-  auto stage = [&](int kt, auto lda, auto ldb) {
+  // each of them had cost issue slots the MFMA pipe waited on).  sa, sb: the
+  // ring slots of A(kt) and B(kt), kt % 3 and kt % 2, compile-time constants
+  // in the unrolled steady state (so no slot arithmetic runs between the
+  // MFMAs) and plain ints elsewhere.
+  auto stage = [&](int kt, auto lda, auto ldb, auto sa, auto sb) {
     constexpr bool LDA = decltype(lda)::value, LDB = decltype(ldb)::value;
-    const SWG_LDS char* as = a_ptr(kt);
-    const SWG_LDS char* bs = b_ptr(kt);
+    const int a0 = sa, b0 = sb;
+    const int a1 = a0 == 2 ? 0 : a0 + 1, a2 = a0 == 0 ? 2 : a0 - 1;  // slots of A(kt+1), A(kt+2)
+    const int b1 = b0 ^ 1;                                            // slot of B(kt+1); B(kt+2) reuses b0
+    const SWG_LDS char* as = a_buf(a0);
+    const SWG_LDS char* bs = b_buf(b0);
     // LDB holds exactly when kt + 2 < nk: then this is not one of the last
     // two stages
     const bool last = LDB ? false : kt + 1 == nk;
@@ -629,10 +647,10 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
     // steps 0 and 1: A(kt+2), half in each (A(2) came with the prologue)
     const i32x4 rA = rs_a(kt + 2);
     step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[0], f[1], 1, acc, wm, wn, lane, [&](int i) {
-      if constexpr (LDA) load_a(rA, kt + 2, i);
+      if constexpr (LDA) load_a_to(rA, kt + 2, a2, i);
     });
     step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[1], f[0], 2, acc, wm, wn, lane, [&](int i) {
-      if constexpr (LDA) load_a(rA, kt + 2, LA / 2 + i);
+      if constexpr (LDA) load_a_to(rA, kt + 2, a2, LA / 2 + i);
     });
     step<T, A_K, B_K, 0>(as, bs, f[0], f[1], 3, acc, wm, wn, lane, no_load);
     // step 3: barrier, then the next stage's first fragments and B(kt+2)
@@ -644,20 +662,30 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
       if (LDB) wait_vmcnt<LA>();
       else wait_vmcnt<0>();
       barrier();
-      nas = a_ptr(kt + 1);
-      nbs = b_ptr(kt + 1);
+      nas = a_buf(a1);
+      nbs = b_buf(b1);
     }
     const i32x4 rB = rs_b(kt + 2);
     step<T, A_K, B_K, LDB ? LB : 0>(nas, nbs, f[1], f[0], 0, acc, wm, wn, lane, [&](int i) {
-      if constexpr (LDB) load_b(rB, kt + 2, i);
+      if constexpr (LDB) load_b_to(rB, kt + 2, b0, i);
     });
   };
   typedef integral_c<true> yes;
   typedef integral_c<false> no;
   int kt = 0;
-  if (nk > 2) stage(kt++, no{}, yes{});         // stage 0: A(2) came with the prologue
-  for (; kt + 2 < nk; ++kt) stage(kt, yes{}, yes{});
-  for (; kt < nk; ++kt) stage(kt, no{}, no{});  // the last two stages load nothing
+  if (nk > 2) stage(kt++, no{}, yes{}, int_c<0>{}, int_c<0>{});  // stage 0: A(2) came with the prologue
+  // from kt = 1 on, six stages per trip: kt % 3 and kt % 2 run through
+  // (1,1) (2,0) (0,1) (1,0) (2,1) (0,0)
+  for (; kt + 7 < nk; kt += 6) {
+    stage(kt, yes{}, yes{}, int_c<1>{}, int_c<1>{});
+    stage(kt + 1, yes{}, yes{}, int_c<2>{}, int_c<0>{});
+    stage(kt + 2, yes{}, yes{}, int_c<0>{}, int_c<1>{});
+    stage(kt + 3, yes{}, yes{}, int_c<1>{}, int_c<0>{});
+    stage(kt + 4, yes{}, yes{}, int_c<2>{}, int_c<1>{});
+    stage(kt + 5, yes{}, yes{}, int_c<0>{}, int_c<0>{});
+  }
+  for (; kt + 2 < nk; ++kt) stage(kt, yes{}, yes{}, kt % 3, kt & 1);
+  for (; kt < nk; ++kt) stage(kt, no{}, no{}, kt % 3, kt & 1);  // the last two stages load nothing
   // Every stage load has been waited for.  The only vector memory reads in
   // flight now are the epilogue prefetches, which must stay in flight: the
   // barriers below are bare s_barriers, not __syncthreads() (whose fence
