@@ -321,6 +321,26 @@ def test_random_shapes_vs_oracle(shape):
         assert_close(name, to_f64(got), ref[name])
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 7, 8, 9, 10, 14, 15, 16, 17, 20])
+def test_k_loop_stage_counts(n):
+    """The GEMM core's K loop runs 64-deep stages: stage 0 (its A operand
+    came with the prologue), six-stage unrolled trips from stage 1 while at
+    least seven more stages follow, single steady stages, then two stages
+    that load nothing.  n stages for F1 (K = D), B1 (K = Dout) and B4 (K = M,
+    ragged) while their N stays a multiple of 256 (the 256x256 tiles); F2,
+    B2 and B3 then see N = 64n or K = 8 and 16 stages on the other tile
+    configurations.  n walks across every boundary of that schedule."""
+    M, D, I, Dout = 64 * n - 5, 64 * n, 512, 64 * n
+    _case("k-loop stages", n, (M, D, I, Dout))
+    _, (x, W1, Wd, dy), (xf, W1f, Wdf, dyf) = _inputs(M, D, I, Dout, seed=100 + n)
+    pre, y = sw.swiglu_mlp_fwd(x, W1, Wd)
+    dx, dW1, dWd = sw.swiglu_mlp_bwd(x, W1, Wd, pre, dy)
+    torch.cuda.synchronize()
+    ref = oracle.backward(xf, W1f, Wdf, dyf)
+    for name, got in (("preact", pre), ("y", y), ("dx", dx), ("dW1", dW1), ("dW_down", dWd)):
+        assert_close(name, to_f64(got), ref[name])
+
+
 def test_empty_batch():
     D, I, Dout = 256, 512, 256
     _case("M=0")
