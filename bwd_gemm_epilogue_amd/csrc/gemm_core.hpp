@@ -295,6 +295,36 @@ __device__ __forceinline__ bf16x8 frag_mn(const SWG_LDS char* t, int r0, int kk,
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// frag_mn's swizzle depends on k % 4 only, and a k16 step moves k by 16, so
+// the byte offset of a lane's read splits into a per-lane part that depends
+// on the fragment's column (the XOR mixes the column's 64 B quarter with the
+// lane's k-row) and a step part kk*16*ROWS*2.  The per-lane parts are
+// computed once per kernel; left inside the loop the compiler rebuilt them
+// for every read (~36 VALU per stage of 64 MFMAs on the MN x MN GEMMs).
+template <int ROWS>
+__device__ __forceinline__ int frag_mn_lane_off(int r0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int e = j >> 2, q = j & 3;
+  const int k = (g >> 1) * 8 + e;
+  const int col = r0 + (g & 1) * 16 + q * 4;
+  return lds_off_mn<ROWS>(k, col >> 3) + (col & 7) * 2;
+}
+// frag_mn of step kk from the per-lane offset: the second read is 4 k-rows on
+template <int ROWS>
+__device__ __forceinline__ bf16x8 frag_mn_at(const SWG_LDS char* t, int off, int kk) {
+  const SWG_LDS char* p = t + off + kk * 16 * ROWS * 2;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWG_LDS i16x4*)p);
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWG_LDS i16x4*)(p + 4 * ROWS * 2));
+  i16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// per-lane offsets of the MN-major fragments (unused for K-major operands)
+template <class T>
+struct MnOff {
+  int a[T::FM], b[T::FN];
+};
+
 template <class T>
 struct Frags {
   bf16x8 a[T::FM], b[T::FN];
@@ -302,15 +332,13 @@ struct Frags {
 
 template <class T, bool A_K, bool B_K>
 __device__ __forceinline__ void load_frags(const SWG_LDS char* As, const SWG_LDS char* Bs, Frags<T>& f, int kk,
-                                           int wm, int wn, int lane) {
+                                           int wm, int wn, int lane, const MnOff<T>& mo) {
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
-    f.a[i] = A_K ? frag_k<T::BK>(As, wm * T::WTM + i * 32, kk, lane)
-                 : frag_mn<T::BM>(As, wm * T::WTM + i * 32, kk, lane);
+    f.a[i] = A_K ? frag_k<T::BK>(As, wm * T::WTM + i * 32, kk, lane) : frag_mn_at<T::BM>(As, mo.a[i], kk);
 #pragma unroll
   for (int j = 0; j < T::FN; ++j)
-    f.b[j] = B_K ? frag_k<T::BK>(Bs, wn * T::WTN + j * 32, kk, lane)
-                 : frag_mn<T::BN>(Bs, wn * T::WTN + j * 32, kk, lane);
+    f.b[j] = B_K ? frag_k<T::BK>(Bs, wn * T::WTN + j * 32, kk, lane) : frag_mn_at<T::BN>(Bs, mo.b[j], kk);
 }
 
 // LDS read instructions per fragment set (transposing reads take two)
@@ -322,13 +350,12 @@ constexpr int frag_reads() {
 // Read fragment i of the next step: A fragments 0..FM-1, then B fragments.
 template <class T, bool A_K, bool B_K>
 __device__ __forceinline__ void read_frag(const SWG_LDS char* As, const SWG_LDS char* Bs, Frags<T>& f, int i,
-                                          int kk, int wm, int wn, int lane) {
+                                          int kk, int wm, int wn, int lane, const MnOff<T>& mo) {
   if (i < T::FM)
-    f.a[i] = A_K ? frag_k<T::BK>(As, wm * T::WTM + i * 32, kk, lane)
-                 : frag_mn<T::BM>(As, wm * T::WTM + i * 32, kk, lane);
+    f.a[i] = A_K ? frag_k<T::BK>(As, wm * T::WTM + i * 32, kk, lane) : frag_mn_at<T::BM>(As, mo.a[i], kk);
   else
     f.b[i - T::FM] = B_K ? frag_k<T::BK>(Bs, wn * T::WTN + (i - T::FM) * 32, kk, lane)
-                         : frag_mn<T::BN>(Bs, wn * T::WTN + (i - T::FM) * 32, kk, lane);
+                         : frag_mn_at<T::BN>(Bs, mo.b[i - T::FM], kk);
 }
 
 // One k16 step with an explicit issue order, slot by slot: the LDS read of
@@ -340,13 +367,14 @@ __device__ __forceinline__ void read_frag(const SWG_LDS char* As, const SWG_LDS 
 template <class T, bool A_K, bool B_K, int NLOAD, class LoadFn>
 __device__ __forceinline__ void step(const SWG_LDS char* As, const SWG_LDS char* Bs, const Frags<T>& cur,
                                      Frags<T>& nxt, int kk_next,
-                                     f32x16 (&acc)[T::FM][T::FN], int wm, int wn, int lane, LoadFn&& ld) {
+                                     f32x16 (&acc)[T::FM][T::FN], int wm, int wn, int lane, const MnOff<T>& mo,
+                                     LoadFn&& ld) {
   constexpr int NF = T::FM + T::FN, NM = T::FM * T::FN;
   constexpr int NS = (NM > NF ? NM : NF) > NLOAD ? (NM > NF ? NM : NF) : NLOAD;
   // load j goes into slot j*NS/NLOAD: evenly spread over the step
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    if (i < NF) read_frag<T, A_K, B_K>(As, Bs, nxt, i, kk_next, wm, wn, lane);
+    if (i < NF) read_frag<T, A_K, B_K>(As, Bs, nxt, i, kk_next, wm, wn, lane, mo);
     if constexpr (NLOAD > 0) {
       if ((i * NLOAD) % NS < NLOAD) ld(i * NLOAD / NS);
     }
@@ -560,13 +588,33 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   auto a_ptr = [&](int j) { return a_buf(j % 3); };
   auto b_ptr = [&](int j) { return b_buf(j & 1); };
   // descriptors: K-major fixed, MN-major rebased at the stage's first k-row
+  // and ending after its k-rows: BK of them except in the last stage.  That
+  // range, rows * ld * 2 bytes, is below 2^28 (ld <= 2^21), so it needs none
+  // of make_rsrc's 64-bit clamps, which in the unrolled loop had cost 64-bit
+  // compares and SGPR spills every stage; the full and last-stage ranges are
+  // computed once and selected per stage with scalar ops (readfirstlane
+  // keeps them in SGPRs: the descriptor operand of the DMA asm is scalar).
+  const int tail_rows = Kg - (nk - 1) * T::BK;  // 1..BK when nk > 0
+  const int mn_full_a = __builtin_amdgcn_readfirstlane(A_K ? 0 : T::BK * (int)g.lda * 2);
+  const int mn_tail_a = __builtin_amdgcn_readfirstlane(A_K ? 0 : tail_rows * (int)g.lda * 2);
+  const int mn_full_b = __builtin_amdgcn_readfirstlane(B_K ? 0 : T::BK * (int)g.ldb * 2);
+  const int mn_tail_b = __builtin_amdgcn_readfirstlane(B_K ? 0 : tail_rows * (int)g.ldb * 2);
+  auto rs_mn = [&](const uint16_t* base, int64_t ld, int full, int tail, int j) -> i32x4 {
+    const uint64_t a = (uint64_t)(base + (int64_t)j * T::BK * ld);
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+    r[2] = j < nk - 1 ? full : (j == nk - 1 ? tail : 0);
+    r[3] = 0x00020000;
+    return r;
+  };
   auto rs_a = [&](int j) -> i32x4 {
     if constexpr (A_K) return ra;
-    else return make_rsrc(Ag + (int64_t)j * T::BK * g.lda, ((int64_t)Kg - (int64_t)j * T::BK) * g.lda * 2);
+    else return rs_mn(Ag, g.lda, mn_full_a, mn_tail_a, j);
   };
   auto rs_b = [&](int j) -> i32x4 {
     if constexpr (B_K) return rb;
-    else return make_rsrc(Bg + (int64_t)j * T::BK * g.ldb, ((int64_t)Kg - (int64_t)j * T::BK) * g.ldb * 2);
+    else return rs_mn(Bg, g.ldb, mn_full_b, mn_tail_b, j);
   };
   // this wave loads blocks wave + 4i; their swizzle classes alternate
   // between those of blocks wave and wave + 4 (K-major) or are all equal
@@ -601,6 +649,17 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   static_assert(PD >= 1, "prefetch depth");
   typename Epi::template Prefetch<T> pf[PD];
   Frags<T> f[2];
+  MnOff<T> mo;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    mo.a[i] = A_K ? 0 : frag_mn_lane_off<T::BM>(wm * T::WTM + i * 32, lane);
+    if constexpr (!A_K) asm volatile("" : "+v"(mo.a[i]));  // kept in a register, not rebuilt per read
+  }
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+    mo.b[j] = B_K ? 0 : frag_mn_lane_off<T::BN>(wn * T::WTN + j * 32, lane);
+    if constexpr (!B_K) asm volatile("" : "+v"(mo.b[j]));
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (j < nk) {
@@ -622,7 +681,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
     else if (nk > 1) wait_vmcnt<LA + LB>();
     else wait_vmcnt<0>();
     barrier();
-    load_frags<T, A_K, B_K>(a_ptr(0), b_ptr(0), f[0], 0, wm, wn, lane);
+    load_frags<T, A_K, B_K>(a_ptr(0), b_ptr(0), f[0], 0, wm, wn, lane, mo);
   }
   // One stage of the K loop.  LDA / LDB: whether it issues A(kt+2) /
   // B(kt+2).  The three variants are chosen once per stage, so the loads
@@ -646,13 +705,13 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
     if (last) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, r0, tn, 0, m_end, g.N, goff}, pf[0], tid);
     // steps 0 and 1: A(kt+2), half in each (A(2) came with the prologue)
     const i32x4 rA = rs_a(kt + 2);
-    step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[0], f[1], 1, acc, wm, wn, lane, [&](int i) {
+    step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[0], f[1], 1, acc, wm, wn, lane, mo, [&](int i) {
       if constexpr (LDA) load_a_to(rA, kt + 2, a2, i);
     });
-    step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[1], f[0], 2, acc, wm, wn, lane, [&](int i) {
+    step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[1], f[0], 2, acc, wm, wn, lane, mo, [&](int i) {
       if constexpr (LDA) load_a_to(rA, kt + 2, a2, LA / 2 + i);
     });
-    step<T, A_K, B_K, 0>(as, bs, f[0], f[1], 3, acc, wm, wn, lane, no_load);
+    step<T, A_K, B_K, 0>(as, bs, f[0], f[1], 3, acc, wm, wn, lane, mo, no_load);
     // step 3: barrier, then the next stage's first fragments and B(kt+2)
     const SWG_LDS char* nas = as;
     const SWG_LDS char* nbs = bs;
@@ -666,7 +725,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
       nbs = b_buf(b1);
     }
     const i32x4 rB = rs_b(kt + 2);
-    step<T, A_K, B_K, LDB ? LB : 0>(nas, nbs, f[1], f[0], 0, acc, wm, wn, lane, [&](int i) {
+    step<T, A_K, B_K, LDB ? LB : 0>(nas, nbs, f[1], f[0], 0, acc, wm, wn, lane, mo, [&](int i) {
       if constexpr (LDB) load_b_to(rB, kt + 2, b0, i);
     });
   };
