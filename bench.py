@@ -68,6 +68,20 @@ def measured_traffic(name: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def measured_mfma(name: str):
+    """MFMA busy and clock of a kernel from a committed rocprofv3 counter
+    pass (profiles/<name>_mfma.json), if it was taken on the current kernel
+    source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{name}_mfma.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    return {k: t[k] for k in ("mfma_busy_pct", "clock_ghz", "pct_of_peak_at_2p4ghz")}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -343,6 +357,7 @@ def main():
     roofline = {"kernel": "bwd_dgrad_fused", "bound": "mfma", "achieved": round(b1_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(b1_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(f"dgrad_fused_{w.name}"),
+                "counters": measured_mfma(f"dgrad_fused_{w.name}"),
                 "algorithmic_flops_per_launch": flops["bwd_dgrad_fused"],
                 "algorithmic_bytes_per_launch": 2 * (M * Dout + I * Dout + 2 * M * 2 * I + M * I)}
 
