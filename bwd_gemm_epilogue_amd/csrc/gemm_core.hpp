@@ -280,27 +280,14 @@ __device__ __forceinline__ bf16x8 frag_k(const SWG_LDS char* t, int r0, int kk, 
 // each group of 16 lanes: lane j receives, in slot e, element j%4 of the 8 B
 // read by lane 4e + j/4.  So lane 4e+q of group g reads k-row (base + e),
 // columns col0 + 4q .. +3, and lane j ends up with column col0 + j, k-rows
-// base .. base+3.  Two reads give the 8 k values.
-template <int ROWS>
-__device__ __forceinline__ bf16x8 frag_mn(const SWG_LDS char* t, int r0, int kk, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int e = j >> 2, q = j & 3;
-  const int k = kk * 16 + (g >> 1) * 8 + e;
-  const int col = r0 + (g & 1) * 16 + q * 4;
-  const int o1 = lds_off_mn<ROWS>(k, col >> 3) + (col & 7) * 2;
-  const int o2 = lds_off_mn<ROWS>(k + 4, col >> 3) + (col & 7) * 2;
-  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWG_LDS i16x4*)(t + o1));
-  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWG_LDS i16x4*)(t + o2));
-  i16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// frag_mn's swizzle depends on k % 4 only, and a k16 step moves k by 16, so
-// the byte offset of a lane's read splits into a per-lane part that depends
-// on the fragment's column (the XOR mixes the column's 64 B quarter with the
-// lane's k-row) and a step part kk*16*ROWS*2.  The per-lane parts are
-// computed once per kernel; left inside the loop the compiler rebuilt them
-// for every read (~36 VALU per stage of 64 MFMAs on the MN x MN GEMMs).
+// base .. base+3.  Two reads, 4 k-rows apart, give the 8 k values.
+//
+// The MN-major swizzle depends on k % 4 only and a k16 step moves k by 16,
+// so the byte offset of a lane's read is a per-lane part, which depends on
+// the fragment's column (the XOR mixes the column's 64 B quarter with the
+// lane's k-row), plus kk*16*ROWS*2.  frag_mn_lane_off gives the per-lane
+// part (kk = 0); the kernel computes it once per fragment, and every read in
+// the K loop is then one register plus an immediate offset.
 template <int ROWS>
 __device__ __forceinline__ int frag_mn_lane_off(int r0, int lane) {
   const int g = lane >> 4, j = lane & 15;
@@ -309,7 +296,7 @@ __device__ __forceinline__ int frag_mn_lane_off(int r0, int lane) {
   const int col = r0 + (g & 1) * 16 + q * 4;
   return lds_off_mn<ROWS>(k, col >> 3) + (col & 7) * 2;
 }
-// frag_mn of step kk from the per-lane offset: the second read is 4 k-rows on
+// the MN-major fragment of step kk from its per-lane offset
 template <int ROWS>
 __device__ __forceinline__ bf16x8 frag_mn_at(const SWG_LDS char* t, int off, int kk) {
   const SWG_LDS char* p = t + off + kk * 16 * ROWS * 2;
