@@ -210,8 +210,10 @@ __device__ __forceinline__ void bstore16(brsrc_t r, uint32_t off, u32x4 v) {
 // no value in it across this code (it sets it right before the few
 // instructions that read it, none of which these kernels use), so it is not
 // restored.
-__device__ __forceinline__ void dma16(const i32x4& rsrc, SWG_LDS char* dst, uint32_t vbase, uint32_t sadd) {
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(uintptr_t)dst);
+// m0: the LDS byte address of the 1 KB destination, a scalar (computed from
+// a hoisted LDS base with scalar arithmetic: a pointer-derived value had been
+// built in VGPRs and moved back with v_readfirstlane for every load).
+__device__ __forceinline__ void dma16(const i32x4& rsrc, int m0, uint32_t vbase, uint32_t sadd) {
   uint32_t voff;
   asm volatile(
       "s_mov_b32 m0, %3\n\t"
@@ -612,13 +614,36 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   const uint32_t vb0 = dma_lane_base<T::BN, B_K>(g.ldb, tn, g.pair_off, wave, lane);
   const uint32_t vb1 = dma_lane_base<T::BN, B_K>(g.ldb, tn, g.pair_off, wave + T::WAVES, lane);
   // load block idx of stage j into ring slot s (s = j % 3 for A, j % 2 for B)
+  // LDS byte address of this wave's first 1 KB block in the ring, a scalar
+  const int lds_wave = __builtin_amdgcn_readfirstlane((int)(uintptr_t)smem) + wave * 1024;
+  // An MN-major operand's block offsets do not change from stage to stage
+  // (its descriptor moves instead), so they are folded into per-block lane
+  // offsets held in VGPRs: as 2 x 8 loop-invariant SGPRs they had pushed the
+  // unrolled loop into SGPR spills (v_readlane reloads every stage).
+  uint32_t vma[LA], vmb[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    vma[i] = A_K ? 0u : ((i & 1) ? va1 : va0) + dma_block_add<T::BM, false>(g.lda, wave + i * T::WAVES, 0);
+    if constexpr (!A_K) asm volatile("" : "+v"(vma[i]));
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    vmb[i] = B_K ? 0u : ((i & 1) ? vb1 : vb0) + dma_block_add<T::BN, false>(g.ldb, wave + i * T::WAVES, 0);
+    if constexpr (!B_K) asm volatile("" : "+v"(vmb[i]));
+  }
   auto load_a_to = [&](const i32x4& r, int j, int s, int idx) {
-    const int b = wave + idx * T::WAVES;
-    dma16(r, a_buf(s) + b * 1024, (idx & 1) ? va1 : va0, dma_block_add<T::BM, A_K>(g.lda, b, A_K ? j * T::BK : 0));
+    const int m0 = lds_wave + s * T::A_BYTES + idx * T::WAVES * 1024;
+    if constexpr (A_K)
+      dma16(r, m0, (idx & 1) ? va1 : va0, dma_block_add<T::BM, true>(g.lda, wave + idx * T::WAVES, j * T::BK));
+    else
+      dma16(r, m0, vma[idx], 0u);
   };
   auto load_b_to = [&](const i32x4& r, int j, int s, int idx) {
-    const int b = wave + idx * T::WAVES;
-    dma16(r, b_buf(s) + b * 1024, (idx & 1) ? vb1 : vb0, dma_block_add<T::BN, B_K>(g.ldb, b, B_K ? j * T::BK : 0));
+    const int m0 = lds_wave + 3 * T::A_BYTES + s * T::B_BYTES + idx * T::WAVES * 1024;
+    if constexpr (B_K)
+      dma16(r, m0, (idx & 1) ? vb1 : vb0, dma_block_add<T::BN, true>(g.ldb, wave + idx * T::WAVES, j * T::BK));
+    else
+      dma16(r, m0, vmb[idx], 0u);
   };
   auto load_a = [&](const i32x4& r, int j, int idx) { load_a_to(r, j, j % 3, idx); };
   auto load_b = [&](const i32x4& r, int j, int idx) { load_b_to(r, j, j & 1, idx); };
