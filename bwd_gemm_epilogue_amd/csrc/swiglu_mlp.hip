@@ -328,12 +328,15 @@ struct SplitPlan {
 // in units of one round of tile work, for S parts per tile:
 //   ceil(rem * S / C) / S                     rounds of 1/S-long workgroups
 //   + 2 * rem * S * 256 KB / (5 TB/s)          partial tiles written and read
-//     / (256 * 256 * K * 2 FLOP / 4.5 TFLOP/s)  one tile's main loop on one CU
-// (the two rates are round figures measured on MI355X).  Unsplit, a last
+//     / (256 * 256 * K * 2 FLOP / 5.5 TFLOP/s)  one tile's main loop on one CU
+// (the two rates are round figures measured on MI355X; a dx round of
+// 256x256x28672 tiles takes ~670 us, 5.6 TFLOP/s per CU).  Unsplit, a last
 // round with few busy units runs faster than a full one: its cost is taken
 // as 0.5 + 0.5 * rem / C (measured: 0.72 with 41% of the units busy).  The S
 // in 2..16 (at most the k-stages) of least cost is kept when it saves at
-// least 20% of that.
+// least 15% of that.  At the 11136 x 3584 x 14336 block this picks S = 2
+// for dx (7 with the 4.5 TFLOP/s figure of a slower core: the whole-step
+// backward measured 40-70 us faster with 2) and keeps the down GEMM's S = 2.
 SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
   SplitPlan pl;
   if (M <= 256 || N % TBig::BN != 0 || K <= 0) return pl;
@@ -342,7 +345,7 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t nst = (K + TBig::BK - 1) / TBig::BK;
   if (full < 1 || rem == 0) return pl;
   const double tile_bytes = (double)TBig::BM * TBig::BN * 4;
-  const double round_us = 2.0 * TBig::BM * TBig::BN * (double)K / 4.5e6;
+  const double round_us = 2.0 * TBig::BM * TBig::BN * (double)K / 5.5e6;
   double best = 1.0;
   int bestS = 1;
   for (int S = 2; S <= 16 && S <= nst; ++S) {
@@ -355,7 +358,7 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
     }
   }
   const double unsplit = 0.5 + 0.5 * (double)rem / kComputeUnits;
-  if (bestS < 2 || best > 0.8 * unsplit) return pl;
+  if (bestS < 2 || best > 0.85 * unsplit) return pl;
   pl.full = (int)(full * kComputeUnits);
   pl.rem = (int)rem;
   pl.S = bestS;

@@ -41,11 +41,12 @@ def test_workspace_sizes():
     M, D, I, Dout = 11136, 3584, 14336, 3584
     tile = 256 * 256 * 4                       # one fp32 partial tile of the split tail
     # 616 tiles of the down GEMM (y = h.W_down) = 2 rounds of 256 + a tail of
-    # 104, split 2 ways; the backward's largest split is dx's tail: 104 tiles, 7 parts
+    # 104, split 2 ways; the backward's splits: dx 104 tiles x 2 parts, dW_down
+    # 16 x 13, dW1 32 x 8 (the largest: 256 partial tiles)
     assert L.swiglu_mlp_fwd_workspace(M, D, I, Dout) == M * I * 2 + 104 * 2 * tile
-    assert L.swiglu_mlp_bwd_workspace(M, D, I, Dout) == M * 2 * I * 2 + M * I * 2 + 104 * 7 * tile
-    assert L.swiglu_mlp_bwd_unfused_workspace(M, D, I, Dout) == M * 2 * I * 2 + 2 * M * I * 2 + 104 * 7 * tile
-    assert L.swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout) == M * 2 * I * 2 + 104 * 7 * tile
+    assert L.swiglu_mlp_bwd_workspace(M, D, I, Dout) == M * 2 * I * 2 + M * I * 2 + 32 * 8 * tile
+    assert L.swiglu_mlp_bwd_unfused_workspace(M, D, I, Dout) == M * 2 * I * 2 + 2 * M * I * 2 + 32 * 8 * tile
+    assert L.swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout) == M * 2 * I * 2 + 32 * 8 * tile
     # whole rounds of tiles (the Llama-like shape): no split tail, no extra bytes
     assert L.swiglu_mlp_fwd_workspace(8192, 4096, 11008, 4096) == 8192 * 11008 * 2
     assert L.swiglu_mlp_bwd_workspace(8192, 4096, 11008, 4096) == 8192 * 2 * 11008 * 2 + 8192 * 11008 * 2
