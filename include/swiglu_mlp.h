@@ -77,13 +77,18 @@ int swiglu_abi_version(void);
  * Whole step
  * ------------------------------------------------------------------------- */
 
-/* Bytes of device workspace swiglu_mlp_fwd needs: the transient h [M,I].
- * Returns 0 for invalid shapes. */
+/* Bytes of device workspace swiglu_mlp_fwd needs: the transient h [M,I], then
+ * fp32 partial sums: those of the down GEMM's split tail when its last round of
+ * 256x256 tiles is split over K (at 11136x3584x14336: 104 tiles x 2 parts, 54.5
+ * MB), or, at 1 <= M <= 16, those of the decode path's split-K GEMMs (a few MB).
+ * Size the workspace with this call; returns 0 for invalid shapes. */
 size_t swiglu_mlp_fwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout);
 
 /* Bytes of device workspace swiglu_mlp_bwd needs: grad_preact [M,2I] and the
- * recomputed h [M,I] (the drop-h report's extra backward buffers).
- * Returns 0 for invalid shapes. */
+ * recomputed h [M,I] (the drop-h report's extra backward buffers), then the fp32
+ * partial tiles of the largest split tail among dW_down, dx and dW1 (at
+ * 11136x3584x14336: dW1's 32 tiles x 8 parts, 67.1 MB).  Size the workspace
+ * with this call; returns 0 for invalid shapes. */
 size_t swiglu_mlp_bwd_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout);
 
 /* Bytes of device workspace swiglu_mlp_bwd_unfused needs: as
@@ -135,8 +140,9 @@ int swiglu_mlp_fwd_save_h(const void* x, const void* W1, const void* W_down,
                           void* preact, void* h, void* y,
                           int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
 
-/* Bytes of device workspace swiglu_mlp_bwd_saved_h needs: grad_preact [M,2I].
- * Returns 0 for invalid shapes. */
+/* Bytes of device workspace swiglu_mlp_bwd_saved_h needs: grad_preact [M,2I],
+ * then the split tails' fp32 partial tiles as for swiglu_mlp_bwd.  Returns 0 for
+ * invalid shapes. */
 size_t swiglu_mlp_bwd_saved_h_workspace(int64_t M, int64_t D, int64_t I, int64_t Dout);
 
 /* Backward from the saved h: the fused dgrad GEMM writes grad_preact only
