@@ -82,6 +82,49 @@ def measured_mfma(name: str):
     return {k: t[k] for k in ("mfma_busy_pct", "clock_ghz", "pct_of_peak_at_2p4ghz")}
 
 
+def fused_dgrad_bytes(M, I, Dout, experts=1):
+    """Algorithmic HBM bytes of one fused dgrad launch, every tensor once in
+    bf16: it reads dy [M,Dout], W_down ([I,Dout] per expert) and preact
+    [M,2I], and writes grad_preact [M,2I] and h [M,I]."""
+    return 2 * (M * Dout + experts * I * Dout + M * 2 * I + M * 2 * I + M * I)
+
+
+def forward_bytes(M, D, I, Dout):
+    """Algorithmic HBM bytes of one forward: reads x [M,D], W1 [D,2I] and
+    W_down [I,Dout], writes preact [M,2I] and y [M,Dout]; the transient h
+    [M,I] is written once and read once."""
+    return 2 * (M * D + D * 2 * I + I * Dout + M * 2 * I + M * Dout + 2 * M * I)
+
+
+def paired_samples(variants, rounds, stream, seed):
+    """The drop-h report's protocol: `rounds` rounds, each running every
+    variant once in a random order, timed with HIP events on `stream`.
+    variants: {name: fn(events)}, where fn records events[0] .. events[k] on
+    `stream` around its parts; returns {name: [[ms of part 0, ...], ...]}."""
+    import torch
+    rnd = random.Random(seed)
+    out = {n: [] for n in variants}
+    for _ in range(rounds):
+        order = list(variants.items())
+        rnd.shuffle(order)
+        for name, fn in order:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            n = fn(ev)
+            ev[n].synchronize()
+            out[name].append([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    return out
+
+
+def paired_summary(a, b, tag_a, tag_b):
+    """Medians of two paired sample lists (one part each), the median paired
+    relative delta (a - b) / b, and the 3% tie rule."""
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    delta = float(np.median((a - b) / b))
+    return {f"{tag_a}_ms_median": round(float(np.median(a)), 4), f"{tag_b}_ms_median": round(float(np.median(b)), 4),
+            "paired_delta": round(delta, 4),
+            "verdict": "tie" if abs(delta) < 0.03 else (f"{tag_a} faster" if delta < 0 else f"{tag_b} faster")}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +134,8 @@ def parse():
     ap.add_argument("--ab-pairs", type=int, default=40)
     ap.add_argument("--stack-layers", type=int, default=4, help="blocks in the stacked workload (0: skip)")
     ap.add_argument("--stack-iters", type=int, default=5)
+    ap.add_argument("--other-workloads", type=int, default=1,
+                    help="also time the fused dgrad at the small and Llama-like shapes and the decode forward (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -218,87 +263,71 @@ def main():
     total_flops = sum(flops.values())
     single_step_ms = float(np.mean([evs[0].elapsed_time(evs[-1]) for evs in evsets]))
 
-    # ---- paired A/B: fused dgrad segment vs dgrad GEMM + elementwise ----
-    ab = None
+    # ---- paired A/B (the drop-h report's protocol: randomly interleaved
+    # rounds, medians, paired delta, < 3% a tie): fused dgrad segment vs
+    # dgrad GEMM + elementwise; the save-h path's fused dgrad (grad_preact
+    # only) vs the drop-h one; the residual epilogues vs the plain GEMMs ----
+    def timed(fn):
+        def run(ev):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            return 1
+        return run
+
+    ab = save_h_ab = residual = None
     if args.ab_pairs > 0:
-        rnd = random.Random(1234)
-        fused_t, unfused_t = [], []
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-
-        def seg_fused():
-            sw.swiglu_bwd_dgrad_fused(dy, Wd, preact, gp, h_bwd)
-
         def seg_unfused():
             sw.swiglu_bwd_dgrad_plain(dy, Wd, dout)
             sw.swiglu_bwd_elementwise(preact, dout, gp, h_bwd)
 
-        for _ in range(3):
-            seg_fused(); seg_unfused()
-        for _ in range(args.ab_pairs):
-            order = [("f", seg_fused), ("u", seg_unfused)]
-            rnd.shuffle(order)
-            res = {}
-            for tag, fn in order:
-                e[0].record(stream)
-                fn()
-                e[1].record(stream)
-                e[1].synchronize()
-                res[tag] = e[0].elapsed_time(e[1])
-            fused_t.append(res["f"])
-            unfused_t.append(res["u"])
-        f_med, u_med = float(np.median(fused_t)), float(np.median(unfused_t))
-        delta = float(np.median((np.array(fused_t) - np.array(unfused_t)) / np.array(unfused_t)))
-        bytes_saved = 2 * M * I * 2
-        ab = {"pairs": args.ab_pairs, "fused_ms_median": round(f_med, 4), "unfused_ms_median": round(u_med, 4),
-              "paired_delta": round(delta, 4), "verdict": "tie" if abs(delta) < 0.03 else (
-                  "fused faster" if delta < 0 else "unfused faster"),
-              "dout_hbm_bytes_avoided": bytes_saved}
-
-    # ---- save-h fallback (the drop-h report's normal MLPBlock): the fused
-    # dgrad without its h store, and what each variant keeps after the forward
-    # alternating pairs, so that both kernels see the same clock and cache state
-    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(10)]
-    for e in ev2:
-        e[0].record(stream)
-        sw.swiglu_bwd_dgrad_fused(dy, Wd, preact, gp, h_bwd)
-        e[1].record(stream)
-        sw.swiglu_bwd_dgrad_fused_gp(dy, Wd, preact, gp)
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    full_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev2]))
-    gp_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev2]))
-    save_h = {"bwd_dgrad_gp_ms": round(gp_ms, 4), "bwd_dgrad_fused_ms_same_pairs": round(full_ms, 4),
-              "bwd_dgrad_gp_tflops": round(flops["bwd_dgrad_fused"] / (gp_ms * 1e-3) / 1e12, 2),
-              "bwd_ms": round(gp_ms + ms["bwd_dw_down"] + ms["bwd_dx"] + ms["bwd_dw1"], 4),
-              "activation_bytes_after_fwd": {"drop_h": 2 * M * 2 * I, "save_h": 2 * M * 2 * I + 2 * M * I},
-              "h_bytes_not_written_in_bwd": 2 * M * I}
-
-    # ---- residual block Y = X + MLP(X): the add in the epilogues of the down
-    # GEMM (y += x) and of the dx GEMM (dx += dy), timed in alternating pairs
-    # against the same GEMMs without it; a separate add would move 3*M*D*2
-    # bytes per tensor through HBM
-    residual = None
-    if D == Dout:
-        ev3 = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(10)]
-        y_res = torch.empty((M, D), dtype=bf, device=dev)
-        dx_res = torch.empty((M, D), dtype=bf, device=dev)
-        for e in ev3:
-            e[0].record(stream)
-            sw.swiglu_fwd_down(h_fwd, Wd, y)
-            e[1].record(stream)
-            sw.swiglu_fwd_down_residual(h_fwd, Wd, x, y_res)
-            e[2].record(stream)
-            sw.swiglu_bwd_dx(gp, W1, dx)
-            e[3].record(stream)
-            sw.swiglu_bwd_dx_residual(gp, W1, dy, dx_res)
-            e[4].record(stream)
+        variants = {
+            "fused": timed(lambda: sw.swiglu_bwd_dgrad_fused(dy, Wd, preact, gp, h_bwd)),
+            "unfused": timed(seg_unfused),
+            "fused_gp_only": timed(lambda: sw.swiglu_bwd_dgrad_fused_gp(dy, Wd, preact, gp)),
+        }
+        if D == Dout:
+            y_res = torch.empty((M, D), dtype=bf, device=dev)
+            dx_res = torch.empty((M, D), dtype=bf, device=dev)
+            variants.update({
+                "down": timed(lambda: sw.swiglu_fwd_down(h_fwd, Wd, y)),
+                "down_residual": timed(lambda: sw.swiglu_fwd_down_residual(h_fwd, Wd, x, y_res)),
+                "dx": timed(lambda: sw.swiglu_bwd_dx(gp, W1, dx)),
+                "dx_residual": timed(lambda: sw.swiglu_bwd_dx_residual(gp, W1, dy, dx_res)),
+            })
+        for fn in variants.values():
+            fn([torch.cuda.Event(enable_timing=True) for _ in range(2)])
         torch.cuda.synchronize()
-        med = [float(np.median([e[k].elapsed_time(e[k + 1]) for e in ev3])) for k in range(4)]
-        residual = {"fwd_down_ms": round(med[0], 4), "fwd_down_residual_ms": round(med[1], 4),
-                    "bwd_dx_ms": round(med[2], 4), "bwd_dx_residual_ms": round(med[3], 4),
-                    "epilogue_add_ms": round(med[1] - med[0] + med[3] - med[2], 4),
-                    "separate_add_hbm_bytes_avoided": 2 * 3 * M * D * 2,
-                    "separate_add_ms_at_hbm_peak": round(2 * 3 * M * D * 2 / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}
+        smp = paired_samples(variants, args.ab_pairs, stream, seed=1234)
+        one = {n: [v[0] for v in smp[n]] for n in smp}
+        ab = {"pairs": args.ab_pairs, **paired_summary(one["fused"], one["unfused"], "fused", "unfused"),
+              "dout_hbm_bytes_avoided": 2 * M * I * 2}
+        gp_only = paired_summary(one["fused_gp_only"], one["fused"], "gp_only", "fused")
+        save_h_ab = {"pairs": args.ab_pairs,
+                  "bwd_dgrad_gp_ms": gp_only["gp_only_ms_median"],
+                  "bwd_dgrad_fused_ms_same_pairs": gp_only["fused_ms_median"],
+                  "paired_delta_gp_only_vs_fused": gp_only["paired_delta"], "verdict": gp_only["verdict"],
+                  "bwd_dgrad_gp_tflops": round(flops["bwd_dgrad_fused"] / (gp_only["gp_only_ms_median"] * 1e-3) / 1e12, 2),
+                  "activation_bytes_after_fwd": {"drop_h": 2 * M * 2 * I, "save_h": 2 * M * 2 * I + 2 * M * I},
+                  "h_bytes_not_written_in_bwd": 2 * M * I}
+        if D == Dout:
+            r_down = paired_summary(one["down_residual"], one["down"], "residual", "plain")
+            r_dx = paired_summary(one["dx_residual"], one["dx"], "residual", "plain")
+            residual = {"pairs": args.ab_pairs,
+                        "fwd_down_ms": r_down["plain_ms_median"], "fwd_down_residual_ms": r_down["residual_ms_median"],
+                        "fwd_down_paired_delta": r_down["paired_delta"],
+                        "bwd_dx_ms": r_dx["plain_ms_median"], "bwd_dx_residual_ms": r_dx["residual_ms_median"],
+                        "bwd_dx_paired_delta": r_dx["paired_delta"],
+                        "epilogue_add_ms": round(r_down["residual_ms_median"] - r_down["plain_ms_median"]
+                                                 + r_dx["residual_ms_median"] - r_dx["plain_ms_median"], 4),
+                        "separate_add_hbm_bytes_avoided": 2 * 3 * M * D * 2,
+                        "separate_add_ms_at_hbm_peak": round(2 * 3 * M * D * 2 / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}
+
+    # ---- one MLP block, drop-h against save-h (the drop-h report's table:
+    # the normal MLPBlock keeps h, drop-h recomputes it), through the
+    # autograd functions: fwd, bwd and full ms in randomly interleaved
+    # rounds, and the memory each keeps after the forward and at its peak ----
+    block = block_compare(sw, x, W1, Wd, dy, args.ab_pairs, stream) if args.ab_pairs > 0 else None
 
     # ---- stack of blocks (the drop-h report's 4-layer stack): forward,
     # backward and full ms through the autograd functions, after-forward and
@@ -359,9 +388,21 @@ def main():
                 "traffic": measured_traffic(f"dgrad_fused_{w.name}"),
                 "counters": measured_mfma(f"dgrad_fused_{w.name}"),
                 "algorithmic_flops_per_launch": flops["bwd_dgrad_fused"],
-                "algorithmic_bytes_per_launch": 2 * (M * Dout + I * Dout + 2 * M * 2 * I + M * I)}
+                "algorithmic_bytes_per_launch": fused_dgrad_bytes(M, I, Dout)}
 
     cpu = cpu_baseline(w, xb, W1b, Wdb, dyb, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    cpu_step = cpu_baseline_step(WORKLOADS["small"], args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    # ---- the other workloads of the measurement plan, in the same run: the
+    # fused dgrad at the small and Llama-like shapes (MFMA roofline) and the
+    # decode-shaped forward (HBM roofline) ----
+    other = None
+    if args.other_workloads:
+        del preact, h_fwd, y, gp, h_bwd, dout, dx, dW1, dWd, wsf, wsb
+        torch.cuda.empty_cache()
+        other = {"dgrad_fused": {n: b1_at(WORKLOADS[n], max(args.steps, 10)) for n in ("small", "llama")}}
+        torch.cuda.empty_cache()
+        other["decode_forward"] = decode_measure(WORKLOADS["decode"], max(args.steps, 20), args.warmup)
 
     out = {
         "metric": "fused dout-GEMM+SwiGLU-bwd TFLOP/s (% MFMA peak); MLP fwd+bwd ms",
@@ -385,23 +426,92 @@ def main():
         "step_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "kernels": {n: {"ms": round(ms[n], 4), "tflops": round(flops[n] / (ms[n] * 1e-3) / 1e12, 2)} for n in names},
         "ab_fused_vs_unfused": ab,
-        "save_h_variant": save_h,
+        "save_h_variant": save_h_ab,
         "residual_block": residual,
+        "block_drop_h_vs_save_h": block,
         "stack": stack,
         "roofline": roofline,
+        "other_workloads": other,
         "cpu_baseline": cpu,
+        "cpu_baseline_step": cpu_step,
         "kernel_source_digest": source_digest(),
     }
     print(json.dumps(out), flush=True)
 
 
+def block_compare(sw, x, W1, Wd, dy, rounds, stream):
+    """One MLP block through the autograd functions, drop-h
+    (SwiGLUMLPFunction: saves {x, W1, W_down, preact}) against save-h
+    (SwiGLUMLPSaveHFunction: also keeps h), as the drop-h report compares
+    them: fwd, bwd and full (fwd + bwd of one sample) ms in `rounds`
+    randomly interleaved rounds with medians and paired deltas, and the
+    allocated MiB above the inputs after the forward and at the peak of
+    fwd + bwd, each taken once from an emptied allocator cache."""
+    import torch
+    xs, W1r, Wdr = (t.clone().requires_grad_(True) for t in (x, W1, Wd))
+    fns = {"drop_h": sw.swiglu_mlp, "save_h": sw.swiglu_mlp_save_h}
+    mem = {}
+    for name, fn in fns.items():
+        for t in (xs, W1r, Wdr):
+            t.grad = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        out = fn(xs, W1r, Wdr)
+        torch.cuda.synchronize()
+        after = torch.cuda.memory_allocated() - base
+        out.backward(dy)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        del out
+        mem[name] = (after, peak)
+
+    def runner(fn):
+        def run(ev):
+            for t in (xs, W1r, Wdr):
+                t.grad = None
+            ev[0].record(stream)
+            out = fn(xs, W1r, Wdr)
+            ev[1].record(stream)
+            out.backward(dy)
+            ev[2].record(stream)
+            return 2
+        return run
+
+    variants = {n: runner(f) for n, f in fns.items()}
+    for v in variants.values():
+        v([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    torch.cuda.synchronize()
+    smp = paired_samples(variants, rounds, stream, seed=4321)
+    res = {"pairs": rounds}
+    for part, idx in (("fwd", 0), ("bwd", 1), ("full", None)):
+        a = [v[idx] if idx is not None else v[0] + v[1] for v in smp["drop_h"]]
+        b = [v[idx] if idx is not None else v[0] + v[1] for v in smp["save_h"]]
+        res[part] = paired_summary(a, b, "drop_h", "save_h")
+    for name, (after, peak) in mem.items():
+        res[f"{name}_after_fwd_MiB"] = round(after / 2**20, 3)
+        res[f"{name}_peak_MiB"] = round(peak / 2**20, 3)
+    res["after_fwd_saving_MiB"] = round((mem["save_h"][0] - mem["drop_h"][0]) / 2**20, 3)
+    del xs, W1r, Wdr
+    return res
+
+
 def _threads():
+    """Threads the oracle's numpy runs on: its BLAS pool (the matrix
+    products are nearly all of the oracle's time; its elementwise work is
+    single-threaded numpy)."""
     try:
         from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("internal_api") in ("openblas", "mkl")]
-        return max(n) if n else os.cpu_count()
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
     except Exception:
-        return os.cpu_count()
+        return 1
+
+
+def _host():
+    return {"host_cpu_count": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "blas_threads": _threads()}
 
 
 def cpu_baseline(w, xb, W1b, Wdb, dyb, budget_s):
@@ -435,7 +545,30 @@ def cpu_baseline(w, xb, W1b, Wdb, dyb, budget_s):
     what = (f"all {rows} token rows, {passes} passes" if rows == w.M else
             f"the first {rows} of {w.M} token rows")
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
-            "sample": f"fused dgrad step (dout GEMM + SwiGLU backward) of {what}, fp64 numpy, {dt:.1f}s"}
+            "sample": f"fused dgrad step (dout GEMM + SwiGLU backward) of {what}, fp64 numpy, {dt:.1f}s",
+            **_host()}
+
+
+def cpu_baseline_step(w, budget_s):
+    """The fp64 oracle of the whole step (forward and backward) at a workload
+    the oracle finishes in seconds, repeated until the time budget is spent;
+    TFLOP/s of the step's GEMMs (6 M D I + 6 M I Dout per step)."""
+    import oracle
+    from workload import bf16_bits_to_f64, make_inputs
+    x, W1, Wd, dy = (bf16_bits_to_f64(a) for a in make_inputs(w))
+    t = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.backward(x, W1, Wd, dy)
+        passes += 1
+        dt = time.perf_counter() - t
+        if dt >= budget_s / 2 or passes >= 50:
+            break
+    fl = (6 * w.M * w.D * w.I + 6 * w.M * w.I * w.Dout) * passes
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "ms_per_step": round(dt * 1e3 / passes, 1),
+            "sample": f"whole fwd+bwd step of the {w.name} workload ({w.M}x{w.D}x{w.I}x{w.Dout}), "
+                      f"{passes} passes, fp64 numpy, {dt:.1f}s", **_host()}
 
 
 def copy_calibration():
@@ -453,10 +586,12 @@ def copy_calibration():
     print(json.dumps({"copy_calibration": {"elements": n, "read_bytes": 2 * n, "write_bytes": 2 * n}}), flush=True)
 
 
-def bench_decode(args, w):
+def decode_measure(w, steps, warmup):
     """Decode-shaped forward (GEMM-1 + SwiGLU epilogue, down GEMM): HBM GB/s
-    of algorithmic bytes.  Weights are rotated over enough copies to exceed
-    the 256 MB last-level cache, so every launch streams them from HBM."""
+    of algorithmic bytes per launch of swiglu_mlp_fwd, mean HIP-event time.
+    Weights are rotated over three copies (1.06 GB at 16 x 4096 x 14336,
+    more than the 256 MB last-level cache), so every launch streams them from
+    HBM."""
     import torch
     import bwd_gemm_epilogue_amd as sw
     from workload import make_inputs
@@ -474,34 +609,72 @@ def bench_decode(args, w):
     preact = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((M, Dout), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(sw.swiglu_mlp_fwd_workspace(M, D, I, Dout), dtype=torch.uint8, device=dev)
-    for k in range(args.warmup):
+    for k in range(warmup):
         sw.swiglu_mlp_fwd(x, W1s[k % copies], Wds[k % copies], preact, y, ws)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         evs[k].record(stream)
         sw.swiglu_mlp_fwd(x, W1s[k % copies], Wds[k % copies], preact, y, ws)
     evs[-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = float(np.mean([evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)]))
-    nbytes = 2 * (M * D + D * 2 * I + M * 2 * I + 2 * M * I + I * Dout + M * Dout)
+    ms = float(np.mean([evs[k].elapsed_time(evs[k + 1]) for k in range(steps)]))
+    nbytes = forward_bytes(M, D, I, Dout)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"fwd_us": round(ms * 1e3, 2), "wall_ms_per_step": round(wall * 1e3 / steps, 4),
+            "gbs": round(gbs, 1), "config": {"workload": f"{w.name} SwiGLU MLP forward", "M": M, "D": D, "I": I,
+                                            "Dout": Dout, "weight_copies_rotated": copies},
+            "roofline": {"kernel": "swiglu_mlp_fwd", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(f"forward_{w.name}"), "algorithmic_bytes_per_launch": nbytes}}
+
+
+def bench_decode(args, w):
+    d = decode_measure(w, args.steps, args.warmup)
     out = {
-        "metric": "decode-shaped SwiGLU MLP forward HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "metric": "decode-shaped SwiGLU MLP forward HBM GB/s", "value": d["gbs"], "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": d["wall_ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{w.name} SwiGLU MLP forward", "M": M, "D": D, "I": I, "Dout": Dout,
-                   "weight_copies_rotated": copies},
-        "roofline": {"kernel": "swiglu_mlp_fwd", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(f"forward_{w.name}"),
-                     "algorithmic_bytes_per_launch": nbytes},
-        "fwd_us": round(ms * 1e3, 2),
+        "config": d["config"], "roofline": d["roofline"], "fwd_us": d["fwd_us"],
     }
     print(json.dumps(out), flush=True)
+
+
+def b1_at(w, iters, warmup=3):
+    """The fused dgrad kernel at another workload's shape: preact from the
+    workload's own x and W1 (GEMM-1 on the GPU), then `iters` launches timed
+    with HIP events; mean ms, TFLOP/s and the fraction of the bf16 peak."""
+    import torch
+    import bwd_gemm_epilogue_amd as sw
+    from workload import make_inputs
+    dev = torch.device("cuda:0")
+
+    def to_dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xb, W1b, Wdb, dyb = make_inputs(w)
+    x, W1, Wd, dy = (to_dev(a) for a in (xb, W1b, Wdb, dyb))
+    preact, _ = sw.swiglu_fwd_gemm1(x, W1)
+    del x, W1
+    gp = torch.empty((w.M, 2 * w.I), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((w.M, w.I), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        sw.swiglu_bwd_dgrad_fused(dy, Wd, preact, gp, h)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    for k in range(iters):
+        ev[k].record(stream)
+        sw.swiglu_bwd_dgrad_fused(dy, Wd, preact, gp, h)
+    ev[-1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[k].elapsed_time(ev[k + 1]) for k in range(iters)]))
+    tf = 2 * w.M * w.Dout * w.I / (ms * 1e-3) / 1e12
+    return {"M": w.M, "D": w.D, "I": w.I, "Dout": w.Dout, "ms": round(ms, 4), "tflops": round(tf, 2),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_bytes_per_launch": fused_dgrad_bytes(w.M, w.I, w.Dout)}
 
 
 def bench_moe(args, w):
@@ -611,7 +784,7 @@ def bench_moe(args, w):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(b1_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(f"dgrad_fused_{w.name}"),
                      "algorithmic_flops_per_launch": b1_flops,
-                     "algorithmic_bytes_per_launch": 2 * (M * Dout + E * I * Dout + 2 * M * 2 * I + M * I)},
+                     "algorithmic_bytes_per_launch": fused_dgrad_bytes(M, I, Dout, experts=E)},
         "cpu_baseline": cpu,
         "kernel_source_digest": source_digest(),
     }
@@ -640,7 +813,7 @@ def cpu_baseline_moe(w, xb, W1b, Wdb, dyb, offb, budget_s):
     fl = 2 * rows * w.Dout * w.I
     return {"value": round(fl / t_total / 1e12, 5), "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
             "sample": f"fused dgrad step of the first {experts} experts ({rows} of {int(offb[-1])} routed rows), "
-                      f"fp64 numpy, {t_total:.1f}s"}
+                      f"fp64 numpy, {t_total:.1f}s", **_host()}
 
 
 if __name__ == "__main__":

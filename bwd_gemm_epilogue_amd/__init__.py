@@ -13,6 +13,8 @@ un-gated "left" branch and [I,2I) the gate, W_down [I,Dout].
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 import re
 
@@ -111,6 +113,103 @@ def exported_names():
     return sorted(set(re.findall(r"\b(swiglu_[a-z0-9_]+)\s*\(", text)))
 
 
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SwiGLUError(fn, status)
+
+
+def _on_device(t: torch.Tensor, name: str):
+    """t must be a contiguous tensor on the GPU the call launches on (the
+    current device inside a call, set from its first tensor)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (no CPU path)")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, the call runs on cuda:{torch.cuda.current_device()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+
+
+def _dev(t: torch.Tensor, name: str, shape=None) -> int:
+    _on_device(t, name)
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    """The HIP stream handle of a call (inside a _launches call `stream` is
+    already the torch stream the call runs on)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _launches(fn):
+    """Run a launching call with its first tensor's device current and the
+    launch stream as torch's current stream.  Every tensor the call
+    allocates (outputs, a temporary workspace) then belongs to that stream in
+    the caching allocator, so a temporary freed on return is not handed to
+    other work before the launched kernels are done with it.  `stream` may
+    be a torch stream or a raw HIP stream handle (wrapped as an external
+    stream)."""
+    params = list(inspect.signature(fn).parameters)
+    at = params.index("stream")
+
+    @functools.wraps(fn)
+    def call(*args, **kw):
+        if len(args) > at:
+            kw["stream"] = args[at]
+            args = args[:at]
+        like = args[0] if args else None
+        if not isinstance(like, torch.Tensor) or not like.is_cuda:
+            raise ValueError(f"{fn.__name__}: the first argument must be a tensor on a GPU (no CPU path)")
+        stream = kw.get("stream")
+        if stream is None:
+            st = torch.cuda.current_stream(like.device)
+        elif isinstance(stream, torch.cuda.Stream):
+            st = stream
+        else:
+            st = torch.cuda.ExternalStream(int(stream), device=like.device)
+        if st.device != like.device:
+            raise ValueError(f"{fn.__name__}: the stream is on {st.device}, the tensors on {like.device}")
+        kw["stream"] = st
+        with torch.cuda.device(like.device), torch.cuda.stream(st):
+            return fn(*args, **kw)
+
+    return call
+
+
+def _empty(shape, like: torch.Tensor):
+    return torch.empty(shape, dtype=torch.bfloat16, device=like.device)
+
+
+def _ws(nbytes: int, like: torch.Tensor, ws):
+    if ws is None:
+        ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+    _on_device(ws, "workspace")
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel() * ws.element_size()} < {nbytes}")
+    return ws
+
+
+def _dims_fwd(x, W1, W_down):
+    M, D = x.shape
+    D2, I2 = W1.shape
+    I, Dout = W_down.shape
+    if D2 != D or I2 != 2 * I:
+        raise ValueError(f"inconsistent shapes x{tuple(x.shape)} W1{tuple(W1.shape)} W_down{tuple(W_down.shape)}")
+    return M, D, I, Dout
+
+
+@_launches
 def swiglu_mlp_fwd_save_h(x, W1, W_down, preact=None, h=None, y=None, stream=None):
     """Save-h forward: returns (preact [M,2I], h [M,I], y [M,Dout]); h is kept."""
     M, D, I, Dout = _dims_fwd(x, W1, W_down)
@@ -127,6 +226,7 @@ def swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout) -> int:
     return lib().swiglu_mlp_bwd_saved_h_workspace(M, D, I, Dout)
 
 
+@_launches
 def swiglu_mlp_bwd_saved_h(x, W1, W_down, preact, h, dy, dx=None, dW1=None, dW_down=None, ws=None,
                            stream=None):
     """Backward from the save-h saved set {x, W1, W_down, preact, h}: (dx, dW1, dW_down)."""
@@ -141,56 +241,6 @@ def swiglu_mlp_bwd_saved_h(x, W1, W_down, preact, h, dy, dx=None, dW1=None, dW_d
         _dev(dW_down, "dW_down", (I, Dout)), ws.data_ptr(), ws.numel() * ws.element_size(),
         M, D, I, Dout, _stream(x, stream)))
     return dx, dW1, dW_down
-
-
-# --------------------------------------------------------------------------
-# marshalling helpers
-# --------------------------------------------------------------------------
-
-def _check(fn: str, status: int):
-    if status != 0:
-        raise SwiGLUError(fn, status)
-
-
-def _dev(t: torch.Tensor, name: str, shape=None) -> int:
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on a GPU (no CPU path)")
-    if t.dtype != torch.bfloat16:
-        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous (row-major)")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    return t.data_ptr()
-
-
-def _stream(t: torch.Tensor, stream) -> int:
-    if stream is None:
-        stream = torch.cuda.current_stream(t.device)
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-
-
-def _empty(shape, like: torch.Tensor):
-    return torch.empty(shape, dtype=torch.bfloat16, device=like.device)
-
-
-def _ws(nbytes: int, like: torch.Tensor, ws):
-    if ws is None:
-        ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
-    if ws.numel() * ws.element_size() < nbytes:
-        raise ValueError(f"workspace too small: {ws.numel() * ws.element_size()} < {nbytes}")
-    return ws
-
-
-def _dims_fwd(x, W1, W_down):
-    M, D = x.shape
-    D2, I2 = W1.shape
-    I, Dout = W_down.shape
-    if D2 != D or I2 != 2 * I:
-        raise ValueError(f"inconsistent shapes x{tuple(x.shape)} W1{tuple(W1.shape)} W_down{tuple(W_down.shape)}")
-    return M, D, I, Dout
 
 
 # --------------------------------------------------------------------------
@@ -221,11 +271,13 @@ def _fwd(fn, x, W1, W_down, preact, y, ws, stream):
     return preact, y
 
 
+@_launches
 def swiglu_mlp_fwd(x, W1, W_down, preact=None, y=None, ws=None, stream=None):
     """Returns (preact [M,2I], y [M,Dout]); h lives only in the workspace."""
     return _fwd("swiglu_mlp_fwd", x, W1, W_down, preact, y, ws, stream)
 
 
+@_launches
 def swiglu_mlp_fwd_residual(x, W1, W_down, preact=None, y=None, ws=None, stream=None):
     """Residual block: returns (preact [M,2I], y = x + MLP(x) [M,D]); needs Dout == D."""
     return _fwd("swiglu_mlp_fwd_residual", x, W1, W_down, preact, y, ws, stream)
@@ -245,12 +297,14 @@ def _bwd(fn, wsfn, x, W1, W_down, preact, dy, dx, dW1, dW_down, ws, stream):
     return dx, dW1, dW_down
 
 
+@_launches
 def swiglu_mlp_bwd(x, W1, W_down, preact, dy, dx=None, dW1=None, dW_down=None, ws=None, stream=None):
     """Fused backward from the saved set {x, W1, W_down, preact}: (dx, dW1, dW_down)."""
     return _bwd("swiglu_mlp_bwd", swiglu_mlp_bwd_workspace, x, W1, W_down, preact, dy,
                 dx, dW1, dW_down, ws, stream)
 
 
+@_launches
 def swiglu_mlp_bwd_residual(x, W1, W_down, preact, dy, dx=None, dW1=None, dW_down=None, ws=None,
                             stream=None):
     """Backward of the residual block: dx includes dy; dW1, dW_down as swiglu_mlp_bwd."""
@@ -258,6 +312,7 @@ def swiglu_mlp_bwd_residual(x, W1, W_down, preact, dy, dx=None, dW1=None, dW_dow
                 dx, dW1, dW_down, ws, stream)
 
 
+@_launches
 def swiglu_mlp_bwd_unfused(x, W1, W_down, preact, dy, dx=None, dW1=None, dW_down=None, ws=None,
                            stream=None):
     """Unfused baseline backward (dout materialised): (dx, dW1, dW_down)."""
@@ -269,6 +324,7 @@ def swiglu_mlp_bwd_unfused(x, W1, W_down, preact, dy, dx=None, dW1=None, dW_down
 # single steps
 # --------------------------------------------------------------------------
 
+@_launches
 def swiglu_fwd_gemm1(x, W1, preact=None, h=None, stream=None):
     M, D = x.shape
     I = W1.shape[1] // 2
@@ -280,6 +336,7 @@ def swiglu_fwd_gemm1(x, W1, preact=None, h=None, stream=None):
     return preact, h
 
 
+@_launches
 def swiglu_fwd_down(h, W_down, y=None, stream=None):
     M, I = h.shape
     Dout = W_down.shape[1]
@@ -290,6 +347,7 @@ def swiglu_fwd_down(h, W_down, y=None, stream=None):
     return y
 
 
+@_launches
 def swiglu_fwd_down_residual(h, W_down, x, y=None, stream=None):
     """y = h.W_down + x with the add in the GEMM epilogue."""
     M, I = h.shape
@@ -301,6 +359,7 @@ def swiglu_fwd_down_residual(h, W_down, x, y=None, stream=None):
     return y
 
 
+@_launches
 def swiglu_bwd_dgrad_fused(dy, W_down, preact, grad_preact=None, h=None, stream=None):
     M, Dout = dy.shape
     I = W_down.shape[0]
@@ -313,6 +372,7 @@ def swiglu_bwd_dgrad_fused(dy, W_down, preact, grad_preact=None, h=None, stream=
     return grad_preact, h
 
 
+@_launches
 def swiglu_bwd_dgrad_fused_gp(dy, W_down, preact, grad_preact=None, stream=None):
     """The save-h path's fused dgrad: grad_preact only."""
     M, Dout = dy.shape
@@ -324,6 +384,7 @@ def swiglu_bwd_dgrad_fused_gp(dy, W_down, preact, grad_preact=None, stream=None)
     return grad_preact
 
 
+@_launches
 def swiglu_bwd_dgrad_plain(dy, W_down, dout=None, stream=None):
     M, Dout = dy.shape
     I = W_down.shape[0]
@@ -334,6 +395,7 @@ def swiglu_bwd_dgrad_plain(dy, W_down, dout=None, stream=None):
     return dout
 
 
+@_launches
 def swiglu_bwd_elementwise(preact, dout, grad_preact=None, h=None, stream=None):
     M, I = dout.shape
     grad_preact = _empty((M, 2 * I), dout) if grad_preact is None else grad_preact
@@ -344,6 +406,7 @@ def swiglu_bwd_elementwise(preact, dout, grad_preact=None, h=None, stream=None):
     return grad_preact, h
 
 
+@_launches
 def swiglu_bwd_dw_down(h, dy, dW_down=None, stream=None):
     M, I = h.shape
     Dout = dy.shape[1]
@@ -354,6 +417,7 @@ def swiglu_bwd_dw_down(h, dy, dW_down=None, stream=None):
     return dW_down
 
 
+@_launches
 def swiglu_bwd_dx(grad_preact, W1, dx=None, stream=None):
     M, I2 = grad_preact.shape
     D = W1.shape[0]
@@ -364,6 +428,7 @@ def swiglu_bwd_dx(grad_preact, W1, dx=None, stream=None):
     return dx
 
 
+@_launches
 def swiglu_bwd_dx_residual(grad_preact, W1, dy, dx=None, stream=None):
     """dx = grad_preact.W1^T + dy with the add in the GEMM epilogue."""
     M, I2 = grad_preact.shape
@@ -375,6 +440,7 @@ def swiglu_bwd_dx_residual(grad_preact, W1, dy, dx=None, stream=None):
     return dx
 
 
+@_launches
 def swiglu_bwd_dw1(x, grad_preact, dW1=None, stream=None):
     M, D = x.shape
     I2 = grad_preact.shape[1]
@@ -385,6 +451,7 @@ def swiglu_bwd_dw1(x, grad_preact, dW1=None, stream=None):
     return dW1
 
 
+@_launches
 def swiglu_act_eval(g, stream=None):
     """sigma, silu, silu' of bf16 g (any shape) as float32 tensors."""
     g = g.contiguous()
@@ -498,7 +565,8 @@ def swiglu_mlp_stack(x, layers, save_h=False):
 # --------------------------------------------------------------------------
 
 def _offsets(off, E: int) -> int:
-    if not isinstance(off, torch.Tensor) or not off.is_cuda or off.dtype != torch.int32 or not off.is_contiguous():
+    _on_device(off, "group_offsets")
+    if off.dtype != torch.int32:
         raise ValueError("group_offsets must be a contiguous int32 tensor on the GPU")
     if tuple(off.shape) != (E + 1,):
         raise ValueError(f"group_offsets has shape {tuple(off.shape)}, expected ({E + 1},)")
@@ -522,6 +590,7 @@ def swiglu_moe_bwd_workspace(M, D, I, Dout, E) -> int:
     return lib().swiglu_moe_bwd_workspace(M, D, I, Dout, E)
 
 
+@_launches
 def swiglu_moe_fwd(x, W1, W_down, group_offsets, preact=None, y=None, ws=None, stream=None):
     """Expert MLPs over expert-packed rows: x [M,D], W1 [E,D,2I], W_down
     [E,I,Dout], group_offsets int32 [E+1] on the GPU.  Returns (preact, y)."""
@@ -536,6 +605,7 @@ def swiglu_moe_fwd(x, W1, W_down, group_offsets, preact=None, y=None, ws=None, s
     return preact, y
 
 
+@_launches
 def swiglu_moe_bwd(x, W1, W_down, group_offsets, preact, dy, dx=None, dW1=None, dW_down=None, ws=None,
                    stream=None):
     """Backward of swiglu_moe_fwd: (dx [M,D], dW1 [E,D,2I], dW_down [E,I,Dout])."""
@@ -552,6 +622,7 @@ def swiglu_moe_bwd(x, W1, W_down, group_offsets, preact, dy, dx=None, dW1=None, 
     return dx, dW1, dW_down
 
 
+@_launches
 def swiglu_moe_bwd_dgrad_fused(dy, W_down, group_offsets, preact, grad_preact=None, h=None, stream=None):
     """The grouped fused dgrad step alone: (grad_preact [M,2I], h [M,I])."""
     M, Dout = dy.shape

@@ -206,10 +206,13 @@ __device__ __forceinline__ void bstore16(brsrc_t r, uint32_t off, u32x4 v) {
 // of hoisting one VGPR per 1 KB block out of the K loop.  M0 holds the LDS
 // base; the v_add between writing M0 and the LDS DMA that reads it is the
 // one wait state the hardware needs there (an s_nop before cost one more
-// issue slot per load).  M0 is a reserved register: the compiler keeps
-// no value in it across this code (it sets it right before the few
-// instructions that read it, none of which these kernels use), so it is not
-// restored.
+// issue slot per load).  M0 is a reserved register, which clang does not
+// accept in a clobber list (it warns that it may not be preserved), so it is
+// written here without one.  That is safe because nothing else in these
+// kernels reads M0: in the compiled library every M0 write is one of these
+// blocks, and no compiler-generated instruction (v_movrel, s_sendmsg, LDS
+// direct, indexed readlane) reads it.  A kernel that added such an
+// instruction would have to set M0 after these loads.
 // m0: the LDS byte address of the 1 KB destination, a scalar (computed from
 // a hoisted LDS base with scalar arithmetic: a pointer-derived value had been
 // built in VGPRs and moved back with v_readfirstlane for every load).

@@ -314,6 +314,23 @@ int run_gemm_auto(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb
 
 constexpr int kComputeUnits = 256;  // MI355X
 
+// Compute units of the current device, queried once per device (0 on a HIP
+// error).  The split-tail and decode plans are worked out for kComputeUnits
+// (the workspace queries stay free of HIP calls); a launch on a device with
+// another count runs unsplit instead (plans_hold()).
+int device_compute_units() {
+  static int cached[64];  // 0 = not yet queried; racing writers store the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+bool plans_hold() { return device_compute_units() == kComputeUnits; }
+
 struct Scratch {
   float* p = nullptr;
   size_t bytes = 0;
@@ -372,7 +389,7 @@ template <bool A_K, bool B_K>
 int run_store_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                    const EpiStore::Params& ep, Scratch sc, hipStream_t st) {
   const SplitPlan pl = split_plan(M, N, K);
-  if (pl.S < 2 || !sc.p || sc.bytes < pl.bytes)
+  if (pl.S < 2 || !sc.p || sc.bytes < pl.bytes || !plans_hold())
     return run_gemm_auto<A_K, B_K, EpiStore>(A, lda, B, ldb, M, N, K, 0, ep, st);
   typedef TBig T;
   GemmArgs g{};
@@ -724,20 +741,9 @@ size_t swiglu_mlp_bwd_unfused_workspace(int64_t M, int64_t D, int64_t I, int64_t
   return swiglu_mlp_bwd_workspace(M, D, I, Dout) + align256((size_t)(M * I * 2));
 }
 
-int swiglu_mlp_fwd(const void* x, const void* W1, const void* W_down, void* preact, void* y, void* ws,
-                   size_t ws_bytes, int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream) {
-  SW_TRY(check_dims(M, D, I, Dout));
-  if (missing(x, M * D) || !W1 || !W_down || missing(preact, M * I) || missing(y, M * Dout))
-    return SWIGLU_ERR_NULL;
-  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned16(preact) || !aligned16(y) ||
-      (ws && !aligned16(ws)))
-    return SWIGLU_ERR_ALIGN;
-  const size_t need = swiglu_mlp_fwd_workspace(M, D, I, Dout);
-  if (need > 0 && (!ws || ws_bytes < need)) return SWIGLU_ERR_WORKSPACE;
-  const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2)};
-  const Range outs[] = {rng(preact, M * 2 * I * 2), rng(y, M * Dout * 2), rng(ws, (int64_t)need)};
-  SW_TRY(check_alias(ins, 3, outs, 3));
-  hipStream_t st = as_stream(stream);
+// The forward after its checks: ws holds at least need bytes.
+static int fwd_launch(const void* x, const void* W1, const void* W_down, void* preact, void* y, void* ws,
+                      size_t need, int64_t M, int64_t D, int64_t I, int64_t Dout, hipStream_t st) {
   if (fwd_is_skinny(M, I, Dout))
     return fwd_skinny(x, W1, W_down, preact, y, ws, (float*)((char*)ws + align256((size_t)(M * I * 2))), M, D, I,
                       Dout, st);
@@ -746,6 +752,29 @@ int swiglu_mlp_fwd(const void* x, const void* W1, const void* W_down, void* prea
   // the split tail's scratch lies inside the checked [ws, ws + need)
   const Scratch sc{(float*)((char*)ws + h_bytes), need - h_bytes};
   return step_down(ws, W_down, y, M, I, Dout, st, sc);
+}
+
+// shapes, null pointers and alignment of the forward's tensors
+static int fwd_check(const void* x, const void* W1, const void* W_down, const void* preact, const void* y, int64_t M,
+                     int64_t D, int64_t I, int64_t Dout) {
+  SW_TRY(check_dims(M, D, I, Dout));
+  if (missing(x, M * D) || !W1 || !W_down || missing(preact, M * I) || missing(y, M * Dout))
+    return SWIGLU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W_down) || !aligned16(preact) || !aligned16(y))
+    return SWIGLU_ERR_ALIGN;
+  return SWIGLU_OK;
+}
+
+int swiglu_mlp_fwd(const void* x, const void* W1, const void* W_down, void* preact, void* y, void* ws,
+                   size_t ws_bytes, int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(fwd_check(x, W1, W_down, preact, y, M, D, I, Dout));
+  if (ws && !aligned16(ws)) return SWIGLU_ERR_ALIGN;
+  const size_t need = swiglu_mlp_fwd_workspace(M, D, I, Dout);
+  if (need > 0 && (!ws || ws_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2)};
+  const Range outs[] = {rng(preact, M * 2 * I * 2), rng(y, M * Dout * 2), rng(ws, (int64_t)need)};
+  SW_TRY(check_alias(ins, 3, outs, 3));
+  return fwd_launch(x, W1, W_down, preact, y, ws, need, M, D, I, Dout, as_stream(stream));
 }
 
 static int bwd_common(bool fused, const void* x, const void* W1, const void* W_down, const void* preact,

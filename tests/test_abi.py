@@ -248,3 +248,30 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sw.swiglu_fwd_down(x, torch.zeros(64, 64, dtype=torch.bfloat16))
+
+
+def test_python_binding_refuses_a_workspace_that_is_not_a_gpu_tensor():
+    """A caller's workspace goes through the same checks as every other
+    tensor: a host tensor (or anything else) is refused before any launch."""
+    import torch
+    like = torch.zeros(4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sw._ws(16, like, torch.zeros(64, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        sw._ws(16, like, bytearray(64))
+
+
+def test_every_launching_binding_runs_inside_a_launch_context():
+    """Every binding that launches kernels takes `stream` and is wrapped so
+    that its allocations belong to the launch stream; each refuses a host
+    tensor as its first argument with ValueError."""
+    import inspect
+    import torch
+    launching = [n for n in sw.__all__ if n.startswith("swiglu_") and callable(getattr(sw, n))
+                 and "stream" in inspect.signature(getattr(sw, n)).parameters]
+    assert len(launching) >= 20
+    for n in launching:
+        f = getattr(sw, n)
+        assert getattr(f, "__wrapped__", None) is not None, f"{n} is not wrapped by _launches"
+        with pytest.raises(ValueError):
+            f(torch.zeros(4, 64, dtype=torch.bfloat16), *([None] * 3))

@@ -59,3 +59,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_bench_byte_ledger_counts_the_tensors_each_step_moves():
+    """bench.py's algorithmic bytes per launch (the roofline's `achieved`
+    for the decode forward, the fused dgrad's byte figure) against the bf16
+    sizes of the arrays the oracle's step functions read and write."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from test_oracle import _ledger_arrays
+    M, D, I, Dout = 97, 64, 160, 48
+    fused, forward, _ = _ledger_arrays(M, D, I, Dout)
+    assert bench.fused_dgrad_bytes(M, I, Dout) == 2 * sum(a.size for a in fused)
+    assert bench.forward_bytes(M, D, I, Dout) == 2 * sum(a.size for a in forward)
+    # grouped over E experts: each expert's W_down is read once
+    E = 5
+    assert bench.fused_dgrad_bytes(M, I, Dout, experts=E) == 2 * sum(a.size for a in fused) + 2 * (E - 1) * I * Dout

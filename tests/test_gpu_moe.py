@@ -170,7 +170,8 @@ def test_moe_autograd_function():
 def test_moe_workload_full_size_matches_dense_per_expert():
     """The MoE workload at its full size (16 experts, 16384 routed rows,
     D = 3584, I = 2048) in the grouped launches the benchmark times, bitwise
-    against the per-expert dense launches (themselves oracle-checked)."""
+    against the per-expert dense launches, and against the fp64 oracle on
+    sampled rows and channels of three experts."""
     w = MOE_WORKLOADS["moe"]
     print("case: moe full size", w, flush=True)
     xb, W1b, Wdb, dyb, off = make_moe_inputs(w, weight_sets=2)
@@ -182,3 +183,27 @@ def test_moe_workload_full_size_matches_dense_per_expert():
     for a, b, n in zip((pre, y, dx, dW1, dWd), ref, ("preact", "y", "dx", "dW1", "dW_down")):
         assert np.array_equal(bits(a), bits(b)), n
     assert torch.isfinite(y.float()).all() and torch.isfinite(dx.float()).all()
+    # the fp64 oracle's exact sampled form on three experts (the smallest,
+    # the median and the largest): 32 of their rows and 32 intermediate
+    # channels, every output on them computed exactly; the per-tensor bound
+    # over the sample
+    counts = np.diff(off)
+    order = np.argsort(counts)
+    I = Wdb.shape[1]
+    for e in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
+        a, b = int(off[e]), int(off[e + 1])
+        rng = np.random.default_rng(100 + e)
+        rows = np.sort(rng.choice(b - a, size=min(32, b - a), replace=False))
+        chans = np.sort(rng.choice(I, size=32, replace=False))
+        s = oracle.sampled_forward_backward(bf16_bits_to_f64(xb[a:b]), bf16_bits_to_f64(W1b[e]),
+                                            bf16_bits_to_f64(Wdb[e]), bf16_bits_to_f64(dyb[a:b]), rows, chans)
+        rt = torch.from_numpy(a + rows).cuda()
+        c2 = torch.from_numpy(np.concatenate([chans, I + chans])).cuda()
+        ct = torch.from_numpy(chans).cuda()
+        print(f"expert {e}: {b - a} rows", flush=True)
+        assert_close("preact rows", to_f64(pre.index_select(0, rt)), s["preact_rows"])
+        assert_close("preact cols", to_f64(pre[a:b].index_select(1, c2)), s["preact_cols"])
+        assert_close("y rows", to_f64(y.index_select(0, rt)), s["y_rows"])
+        assert_close("dx rows", to_f64(dx.index_select(0, rt)), s["dx_rows"])
+        assert_close("dW1 cols", to_f64(dW1[e].index_select(1, c2)), s["dW1_cols"])
+        assert_close("dW_down rows", to_f64(dWd[e].index_select(0, ct)), s["dW_down_rows"])

@@ -385,3 +385,31 @@ def test_autograd_function_saves_four_tensors():
     assert np.array_equal(bits(x3.grad.reshape(-1, D)), bits(dx))
     assert np.array_equal(bits(W1r.grad), bits(dW1))
     assert np.array_equal(bits(Wdr.grad), bits(dWd))
+
+
+def test_side_stream_and_workspace_checks():
+    """A call on a stream that is not the current one (torch stream or raw
+    handle): its outputs and temporary workspace belong to that stream, so
+    allocations made meanwhile on the current stream cannot take them over;
+    results equal the current-stream call bit for bit.  A workspace that is
+    a stride-0 view (its numel overstates its storage) is refused."""
+    M, D, I, Dout = 300, 512, 768, 512
+    _case("side stream", (M, D, I, Dout))
+    _, (x, W1, Wd, dy), _ = _inputs(M, D, I, Dout, seed=21)
+    pre, y = sw.swiglu_mlp_fwd(x, W1, Wd)
+    ref = [bits(t) for t in sw.swiglu_mlp_bwd(x, W1, Wd, pre, dy)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for handle in (side, side.cuda_stream):
+        side.wait_stream(torch.cuda.current_stream())
+        got = sw.swiglu_mlp_bwd(x, W1, Wd, pre, dy, stream=handle)
+        # allocations on the current stream while the side stream may still run
+        junk = [torch.full((1 << 22,), 7, dtype=torch.uint8, device="cuda") for _ in range(8)]
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, bits(b))
+        del junk
+    ws = torch.zeros(1, dtype=torch.uint8, device="cuda").expand(1 << 30)
+    with pytest.raises(ValueError):
+        sw.swiglu_mlp_bwd(x, W1, Wd, pre, dy, ws=ws)

@@ -431,3 +431,29 @@ def test_drop_h_memory_saving_is_one_h():
     stack = _golden()["drop_h_stack_MiB"]
     assert abs(stack["after_forward_normal"] - stack["after_forward_drop_h"]
                - stack["layers"] * gold["saving"]) < 1e-9
+
+
+def _ledger_arrays(M, D, I, Dout, seed=3):
+    """The arrays each step reads and writes, as the oracle's own step
+    functions take and return them (every dimension distinct, so that a
+    term with a wrong or swapped dimension changes the count)."""
+    rng = np.random.default_rng(seed)
+    x, W1, Wd, dy = (rng.standard_normal(s) for s in ((M, D), (D, 2 * I), (I, Dout), (M, Dout)))
+    pre, h, y = oracle.forward(x, W1, Wd)
+    dout = dy @ Wd.T
+    gp, h_bwd = oracle.swiglu_bwd_elementwise(pre, dout)
+    fused = [dy, Wd, pre, gp, h_bwd]                # reads dy, W_down, preact; writes grad_preact, h
+    forward = [x, W1, Wd, pre, y, h, h]             # h written once and read once
+    return fused, forward, dout
+
+
+def test_byte_ledger_totals_count_the_tensors_each_step_moves():
+    """algorithmic_bytes totals against an independent count: the bf16 sizes
+    of the arrays the oracle's own step functions read and write."""
+    M, D, I, Dout = 97, 64, 160, 48
+    fused, forward, dout = _ledger_arrays(M, D, I, Dout)
+    b = oracle.algorithmic_bytes(M, D, I, Dout)
+    assert b["fused_dgrad"] == 2 * sum(a.size for a in fused)
+    assert b["forward"] == 2 * sum(a.size for a in forward)
+    assert b["unfused_dgrad"] == b["fused_dgrad"] + 2 * 2 * dout.size   # dout written and read back
+    assert b["saved"] == 2 * 2 * dout.size

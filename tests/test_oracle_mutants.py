@@ -23,6 +23,7 @@ _sigmoid, _backward = osw.sigmoid, osw.backward
 _bwd_elem, _fwd_elem = osw.swiglu_bwd_elementwise, osw.swiglu_fwd_elementwise
 _moe_backward, _stack_backward = osw.moe_backward, osw.stack_backward
 _backward_residual, _sampled = osw.backward_residual, osw.sampled_forward_backward
+_bytes = osw.algorithmic_bytes
 
 
 def _sigmoid_sign_flipped(g):
@@ -115,6 +116,19 @@ def _sampled_rows_reversed(x, W1, Wd, dy, rows, chans):
     return r
 
 
+def _bytes_fused_without_h(M, D, I, Dout, elem=2):
+    b = _bytes(M, D, I, Dout, elem)
+    b["fused_dgrad"] -= elem * M * I
+    b["unfused_dgrad"] -= elem * M * I
+    return b
+
+
+def _bytes_forward_h_once(M, D, I, Dout, elem=2):
+    b = _bytes(M, D, I, Dout, elem)
+    b["forward"] -= elem * M * I
+    return b
+
+
 MUTANTS = {
     "sigmoid with the exponent's sign flipped": {"sigmoid": _sigmoid_sign_flipped},
     "silu without its sigma factor": {"silu": _silu_without_sigma},
@@ -131,6 +145,8 @@ MUTANTS = {
     "stack gradients in reversed layer order": {"stack_backward": _stack_layers_reversed},
     "MoE dW1 given to the wrong expert": {"moe_backward": _moe_wrong_expert},
     "sampled dW_down rows misordered": {"sampled_forward_backward": _sampled_rows_reversed},
+    "fused dgrad bytes without the h store": {"algorithmic_bytes": _bytes_fused_without_h},
+    "forward bytes with h moved once": {"algorithmic_bytes": _bytes_forward_h_once},
 }
 
 
