@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "SwiGLUError", "lib", "LIB_PATH", "HEADER_PATH", "exported_names",
     "swiglu_mlp_fwd", "swiglu_mlp_bwd", "swiglu_mlp_bwd_unfused",
+    "swiglu_mlp_fwd_noalloc", "swiglu_mlp_fwd_noalloc_limit",
     "swiglu_mlp_fwd_workspace", "swiglu_mlp_bwd_workspace", "swiglu_mlp_bwd_unfused_workspace",
     "swiglu_fwd_gemm1", "swiglu_fwd_down", "swiglu_bwd_dgrad_fused", "swiglu_bwd_dgrad_plain",
     "swiglu_bwd_elementwise", "swiglu_bwd_dw_down", "swiglu_bwd_dx", "swiglu_bwd_dw1",
@@ -51,6 +52,8 @@ _SIGNATURES = {
     "swiglu_mlp_bwd_workspace": (_SZ, [_I64] * 4),
     "swiglu_mlp_bwd_unfused_workspace": (_SZ, [_I64] * 4),
     "swiglu_mlp_fwd": (ctypes.c_int, [_P] * 5 + [_P, _SZ] + [_I64] * 4 + [_P]),
+    "swiglu_mlp_fwd_noalloc_limit": (_SZ, []),
+    "swiglu_mlp_fwd_noalloc": (ctypes.c_int, [_P] * 5 + [_I64] * 4 + [_P]),
     "swiglu_mlp_bwd": (ctypes.c_int, [_P] * 8 + [_P, _SZ] + [_I64] * 4 + [_P]),
     "swiglu_mlp_bwd_unfused": (ctypes.c_int, [_P] * 8 + [_P, _SZ] + [_I64] * 4 + [_P]),
     "swiglu_fwd_gemm1": (ctypes.c_int, [_P] * 4 + [_I64] * 3 + [_P]),
@@ -275,6 +278,26 @@ def _fwd(fn, x, W1, W_down, preact, y, ws, stream):
 def swiglu_mlp_fwd(x, W1, W_down, preact=None, y=None, ws=None, stream=None):
     """Returns (preact [M,2I], y [M,Dout]); h lives only in the workspace."""
     return _fwd("swiglu_mlp_fwd", x, W1, W_down, preact, y, ws, stream)
+
+
+def swiglu_mlp_fwd_noalloc_limit() -> int:
+    """Bytes of the library's static workspace used by swiglu_mlp_fwd_noalloc."""
+    return lib().swiglu_mlp_fwd_noalloc_limit()
+
+
+@_launches
+def swiglu_mlp_fwd_noalloc(x, W1, W_down, preact=None, y=None, stream=None):
+    """swiglu_mlp_fwd without a workspace argument: the library's own static
+    device array holds h and the partial sums, so the C call allocates
+    nothing (outputs are allocated here only when not given).  Refuses
+    shapes whose workspace exceeds swiglu_mlp_fwd_noalloc_limit()."""
+    M, D, I, Dout = _dims_fwd(x, W1, W_down)
+    preact = _empty((M, 2 * I), x) if preact is None else preact
+    y = _empty((M, Dout), x) if y is None else y
+    _check("swiglu_mlp_fwd_noalloc", lib().swiglu_mlp_fwd_noalloc(
+        _dev(x, "x"), _dev(W1, "W1"), _dev(W_down, "W_down"),
+        _dev(preact, "preact", (M, 2 * I)), _dev(y, "y", (M, Dout)), M, D, I, Dout, _stream(x, stream)))
+    return preact, y
 
 
 @_launches

@@ -10,6 +10,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gemm_core.hpp"
 #include "skinny.hpp"
 #include "swiglu_math.hpp"
@@ -208,6 +210,14 @@ __global__ void __launch_bounds__(256) zero_kernel(u32x4* __restrict__ p, int64_
 // ===========================================================================
 // Host side
 // ===========================================================================
+
+// Workspace of the no-allocation forward (swiglu_mlp_fwd_noalloc): the HIP
+// runtime places one copy on each GPU that loads this library, kept until
+// the process ends.  32 MiB holds h and the split-K partial sums of the
+// decode-shaped forward (about 4.2 MB at 16 x 4096 x 14336) with room.
+constexpr size_t kStaticWsBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticWsBytes];
+
 namespace {
 
 using namespace swg;
@@ -696,6 +706,29 @@ int moe_dw1(const void* x, const void* gp, const int* off, void* dW1, int64_t M,
 
 int check_experts(int64_t E) { return E < 1 ? SWIGLU_ERR_SHAPE : (E > 65536 ? SWIGLU_ERR_UNSUPPORTED : SWIGLU_OK); }
 
+// --- the no-allocation forward's workspace --------------------------------
+// `scratch` (file scope, above) is a library-owned device array per GPU.
+// Its name is a host-side stand-in: host code uses only the device address
+// hipGetSymbolAddress returns for the current device, taken once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (first call on a device: with
+// that device current, hipGetSymbolAddress, checked).
+int static_workspace(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SWIGLU_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SWIGLU_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SWIGLU_OK;
+}
+
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 }  // namespace
@@ -719,7 +752,7 @@ const char* swiglu_status_string(int status) {
   }
 }
 
-int swiglu_abi_version(void) { return (1 << 16) | 3; }
+int swiglu_abi_version(void) { return (1 << 16) | 4; }
 
 // Workspace layouts (each part 256-byte aligned):
 //   forward          h [M,I] | skinny partial sums or the down GEMM's split tail
@@ -774,6 +807,21 @@ int swiglu_mlp_fwd(const void* x, const void* W1, const void* W_down, void* prea
   const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2)};
   const Range outs[] = {rng(preact, M * 2 * I * 2), rng(y, M * Dout * 2), rng(ws, (int64_t)need)};
   SW_TRY(check_alias(ins, 3, outs, 3));
+  return fwd_launch(x, W1, W_down, preact, y, ws, need, M, D, I, Dout, as_stream(stream));
+}
+
+size_t swiglu_mlp_fwd_noalloc_limit(void) { return kStaticWsBytes; }
+
+int swiglu_mlp_fwd_noalloc(const void* x, const void* W1, const void* W_down, void* preact, void* y, int64_t M,
+                           int64_t D, int64_t I, int64_t Dout, void* stream) {
+  SW_TRY(fwd_check(x, W1, W_down, preact, y, M, D, I, Dout));
+  const size_t need = swiglu_mlp_fwd_workspace(M, D, I, Dout);
+  if (need > kStaticWsBytes) return SWIGLU_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, M * D * 2), rng(W1, D * 2 * I * 2), rng(W_down, I * Dout * 2)};
+  const Range outs[] = {rng(preact, M * 2 * I * 2), rng(y, M * Dout * 2)};
+  SW_TRY(check_alias(ins, 3, outs, 2));
+  void* ws = nullptr;
+  SW_TRY(static_workspace(&ws));
   return fwd_launch(x, W1, W_down, preact, y, ws, need, M, D, I, Dout, as_stream(stream));
 }
 

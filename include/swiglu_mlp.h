@@ -31,8 +31,10 @@
  *     No output may overlap an input or another output.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as
  *     void*; NULL means the default stream).  The library never allocates
- *     device memory, never synchronises and never prints.  Device faults
- *     surface at the caller's next synchronisation.
+ *     device memory (its one static device array, the workspace of
+ *     swiglu_mlp_fwd_noalloc, is placed by the HIP runtime when the library
+ *     is loaded on a device), never synchronises and never prints.  Device
+ *     faults surface at the caller's next synchronisation.
  *   - Shapes: M (tokens) >= 0; D, I and Dout are positive multiples of 64.
  *     With M == 0 the forward outputs are empty and dW1 and dW_down are
  *     written as zeros (a sum over no tokens).
@@ -70,7 +72,7 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* swiglu_status_string(int status);
 
-/* ABI version of this header, (major << 16) | minor: 1.3. */
+/* ABI version of this header, (major << 16) | minor: 1.4. */
 int swiglu_abi_version(void);
 
 /* ---------------------------------------------------------------------------
@@ -132,6 +134,27 @@ int swiglu_mlp_bwd_unfused(const void* x, const void* W1, const void* W_down,
  * Same arithmetic as the drop-h calls; the saved set is {x, W1, W_down,
  * preact, h}, so the backward's dgrad epilogue writes grad_preact only.
  * ------------------------------------------------------------------------- */
+
+/* No-allocation forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and results as swiglu_mlp_fwd without
+ * ws / ws_bytes: the workspace (h and the split-K partial sums) is a
+ * library-owned static device array of swiglu_mlp_fwd_noalloc_limit() bytes
+ * (32 MiB) on each GPU, placed when the library is loaded on that GPU and
+ * kept until the process ends; the first call on a device looks up its
+ * address there.  Shapes whose swiglu_mlp_fwd_workspace exceeds the limit
+ * (e.g. M * I * 2 > 32 MiB) are refused with SWIGLU_ERR_WORKSPACE before any
+ * HIP call; the decode-shaped forward (M <= 16) needs about 4 MB at
+ * D = 4096, I = 14336.  Nothing is read from the array before this call
+ * writes it, so no clearing is needed.  Every call on one GPU uses that
+ * GPU's one array: calls that may overlap on one GPU (on different streams
+ * without ordering between them) race and must not be made.  Errors as
+ * swiglu_mlp_fwd, plus SWIGLU_ERR_HIP if the array's address cannot be
+ * obtained. */
+size_t swiglu_mlp_fwd_noalloc_limit(void);
+int swiglu_mlp_fwd_noalloc(const void* x, const void* W1, const void* W_down,
+                           void* preact, void* y,
+                           int64_t M, int64_t D, int64_t I, int64_t Dout, void* stream);
 
 /* Forward that keeps h: as swiglu_mlp_fwd, but h [M,I] is written to the
  * caller's `h` (part of the saved set) and no workspace is used (any M takes

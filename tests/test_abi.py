@@ -275,3 +275,25 @@ def test_every_launching_binding_runs_inside_a_launch_context():
         assert getattr(f, "__wrapped__", None) is not None, f"{n} is not wrapped by _launches"
         with pytest.raises(ValueError):
             f(torch.zeros(4, 64, dtype=torch.bfloat16), *([None] * 3))
+
+
+def test_noalloc_forward_refuses_shapes_beyond_its_static_workspace():
+    """The no-allocation forward: the limit is its stated 32 MiB; a shape
+    whose workspace fits is checked like swiglu_mlp_fwd (bad arguments are
+    refused on the host), and one whose workspace exceeds the limit is
+    refused with SWIGLU_ERR_WORKSPACE before any HIP call."""
+    L = sw.lib()
+    limit = L.swiglu_mlp_fwd_noalloc_limit()
+    assert limit == 32 * MB
+    f = L.swiglu_mlp_fwd_noalloc
+    # decode shape fits
+    assert L.swiglu_mlp_fwd_workspace(16, 4096, 14336, 4096) <= limit
+    # h alone past the limit: M * I * 2 > 32 MiB
+    M, D, I, Dout = 4096, 256, 8192, 256
+    assert L.swiglu_mlp_fwd_workspace(M, D, I, Dout) > limit
+    assert f(addr(0), addr(1), addr(2), addr(3), addr(4), M, D, I, Dout, None) == WS
+    # the forward's other checks, before the workspace one
+    assert f(addr(0), addr(1), addr(2), addr(3), addr(4), 16, 100, 512, 256, None) == UNSUP
+    assert f(addr(0), None, addr(2), addr(3), addr(4), 16, 256, 512, 256, None) == NULL
+    assert f(addr(0) + 8, addr(1), addr(2), addr(3), addr(4), 16, 256, 512, 256, None) == ALIGN
+    assert f(addr(0), addr(1), addr(2), addr(0), addr(4), 16, 256, 512, 256, None) == ALIAS
