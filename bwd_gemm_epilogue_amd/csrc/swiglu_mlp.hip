@@ -226,6 +226,8 @@ using namespace swg;
 typedef TileCfg<256, 256, 2, 2, 64> TBig;  // 4 waves, 128x128 per wave, 160 KB LDS ring
 typedef TileCfg<128, 128, 2, 2, 64> TMid;    // 4 waves, 64x64 per wave
 typedef TileCfg<64, 64, 2, 2, 64> TSmall;      // 4 waves, 32x32 per wave (N % 128 != 0)
+typedef TileCfg<256, 128, 2, 2, 64> TWide;   // 4 waves, 128x64 per wave
+typedef TileCfg<128, 256, 2, 2, 64> TTall;   // 4 waves, 64x128 per wave
 
 // D, I, Dout limit: keeps every in-tile byte offset of a 256-row tile below 2^31
 constexpr int64_t kMaxDim = (int64_t)1 << 20;
@@ -340,6 +342,62 @@ int device_compute_units() {
 }
 
 bool plans_hold() { return device_compute_units() == kComputeUnits; }
+
+// --- tile shape of the dout GEMMs (K-major dy and W_down) ------------------
+// A launch of T tiles on C compute units runs floor(T / C) full rounds and
+// a last round of T mod C tiles, whose cost is taken as 0.5 + 0.5 * (T mod
+// C) / C of a round (the split-tail model below).  Each tile shape works at
+// its own rate per compute unit, measured on the fused dgrad with the same
+// k-loop relative to 256 x 256 tiles: 256 x 128 0.945, 128 x 256 0.903,
+// 128 x 128 0.723.  The shape of least (rounds x tile area / rate) is used:
+// at 11136 x 14336 (K 3584) and 8192 x 11008 (K 4096) that is 256 x 256
+// (measured best or tied); at 2048 x 2816, 4096 x 5632 and 11136 x 1792 a
+// 256- or 128-row half-size tile (measured 1.53x, 1.12x and 1.13x faster).
+enum KkTile { kTileBig, kTileWide, kTileTall, kTileMid, kTileSmall };
+
+KkTile pick_kk_tile(int64_t M, int64_t N, int cus) {
+  if (N % 128 != 0) return kTileSmall;
+  struct Cand {
+    KkTile k;
+    int bm, bn;
+    double rate;
+  };
+  const Cand cands[] = {{kTileBig, 256, 256, 1.0},
+                        {kTileWide, 256, 128, 0.945},
+                        {kTileTall, 128, 256, 0.903},
+                        {kTileMid, 128, 128, 0.723}};
+  const int64_t C = cus > 0 ? cus : 256;
+  KkTile best = kTileMid;
+  double best_cost = 0.0;
+  bool any = false;
+  for (const Cand& c : cands) {
+    if (N % c.bn != 0) continue;
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * (N / c.bn);
+    const int64_t full = tiles / C, rem = tiles % C;
+    const double rounds = (double)full + (rem > 0 ? 0.5 + 0.5 * (double)rem / (double)C : 0.0);
+    const double cost = rounds * c.bm * c.bn / c.rate;
+    if (!any || cost < best_cost - 1e-9) {
+      best = c.k;
+      best_cost = cost;
+      any = true;
+    }
+  }
+  return best;
+}
+
+// A K-major x K-major GEMM (the dout GEMM and its plain-store twin) in the
+// tile shape pick_kk_tile chooses.
+template <class Epi>
+int run_gemm_kk(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                const typename Epi::Params& ep, hipStream_t st) {
+  switch (pick_kk_tile(M, N, device_compute_units())) {
+    case kTileBig: return run_gemm<TBig, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
+    case kTileWide: return run_gemm<TWide, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
+    case kTileTall: return run_gemm<TTall, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
+    case kTileMid: return run_gemm<TMid, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
+    default: return run_gemm<TSmall, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
+  }
+}
 
 struct Scratch {
   float* p = nullptr;
@@ -523,7 +581,7 @@ int step_down(const void* h, const void* Wd, void* y, int64_t M, int64_t I, int6
 int step_dgrad_fused(const void* dy, const void* Wd, const void* preact, void* gp, void* h, int64_t M, int64_t I,
                      int64_t Dout, hipStream_t st) {
   EpiSwigluBwd::Params ep{cu16(preact), u16(gp), u16(h), I};
-  return run_gemm_auto<true, true, EpiSwigluBwd>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, 0, ep, st);
+  return run_gemm_kk<EpiSwigluBwd>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, ep, st);
 }
 
 // residual-add epilogues (Lesson 24, section 24): y = x + h.W_down and, in
@@ -543,13 +601,13 @@ int step_dx_residual(const void* gp, const void* W1, const void* dy, void* dx, i
 int step_dgrad_fused_gp(const void* dy, const void* Wd, const void* preact, void* gp, int64_t M, int64_t I,
                         int64_t Dout, hipStream_t st) {
   EpiSwigluBwdGp::Params ep{cu16(preact), u16(gp), nullptr, I};
-  return run_gemm_auto<true, true, EpiSwigluBwdGp>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, 0, ep, st);
+  return run_gemm_kk<EpiSwigluBwdGp>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, ep, st);
 }
 
 int step_dgrad_plain(const void* dy, const void* Wd, void* dout, int64_t M, int64_t I, int64_t Dout,
                      hipStream_t st) {
   EpiStore::Params ep{u16(dout), I};
-  return run_gemm_auto<true, true, EpiStore>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, 0, ep, st);
+  return run_gemm_kk<EpiStore>(cu16(dy), Dout, cu16(Wd), Dout, M, I, Dout, ep, st);
 }
 
 int step_elementwise(const void* preact, const void* dout, void* gp, void* h, int64_t M, int64_t I, hipStream_t st) {
