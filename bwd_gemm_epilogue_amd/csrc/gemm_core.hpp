@@ -160,8 +160,15 @@ struct int_c {
 // num_records = bytes, dword 3 = 0x00020000 (32-bit data format, as gfx9
 // expects for untyped access).  The range check zero-fills any 16 B load at
 // or past `bytes` (all offsets and ranges here are multiples of 16 B).
+// The byte count is clamped into [0, 0x7FFFFFF0] with 32-bit compares, which
+// stay scalar for a uniform count (a 64-bit compare is a vector instruction
+// that holds its constant in a VGPR pair).
+__device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
+  const uint32_t hi = (uint32_t)((uint64_t)bytes >> 32), lo = (uint32_t)bytes;
+  return (int32_t)hi < 0 ? 0u : ((hi != 0u || lo > 0x7FFFFFF0u) ? 0x7FFFFFF0u : lo);
+}
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0ll : bytes);
+  const uint32_t n = clamp_records(bytes);
   const uint64_t a = (uint64_t)base;
   i32x4 r;
   r[0] = (int)(uint32_t)a;
@@ -182,8 +189,7 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
 // spans at most 256 rows of at most 2^21 elements.
 typedef __amdgpu_buffer_rsrc_t brsrc_t;
 __device__ __forceinline__ brsrc_t rows_rsrc(const void* base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0ll : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)clamp_records(bytes), 0x00020000);
 }
 // an offset past every num_records above: the access is dropped
 constexpr uint32_t kOffOutOfRange = 0x80000000u;
@@ -466,12 +472,39 @@ struct SlabCtx {
   __device__ __forceinline__ int row(int sr) const {
     return r0 + (sr >> 5) * T::WTM + s * 32 + (sr & 31);
   }
+  // The epilogues walk a slab in 8-column chunks: a thread's item k is slab
+  // row q + k * P, chunk ch, with q = tid / CPR and ch = tid % CPR (CPR
+  // chunks per row, P rows per pass of the workgroup).  Since P divides 32,
+  // that row lies item_row(k) + q rows below the tile's first row, and
+  // item_row(k) is a constant once k and s are (unrolled loops): each item's
+  // address is then a per-thread base plus a scalar product.
+  static constexpr int CPR = T::BN / 8, P = T::THREADS / CPR;
+  static_assert(T::THREADS % CPR == 0 && 32 % P == 0, "item rows must split into q + item_row(k)");
+  __device__ __forceinline__ int item_row(int k) const {
+    return ((k * P) >> 5) * T::WTM + s * 32 + ((k * P) & 31);
+  }
   __device__ __forceinline__ f32x8 read8(int sr, int c) const {
     const SWG_LDS f32x4* p = (const SWG_LDS f32x4*)(slab + sr * T::SLAB_LD + c);
     f32x4 lo = p[0], hi = p[1];
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
+
+// The epilogue reads issued while slabs are processed: read e (item e % NI of
+// slab PRE + e / NI) goes out during apply(a), a the smallest with
+// e < ceil(E (a + 1) / A).  It must be issued before its slab is processed
+// (a < slab) and into registers whose previous slab, slab - PD, is done
+// (a > slab - PD).
+template <int E, int A, int NI, int PRE, int PD>
+constexpr bool epi_schedule_ok() {
+  for (int e = 0; e < E; ++e) {
+    int a = 0;
+    while (!(e < (E * (a + 1) + A - 1) / A)) ++a;
+    const int slab = PRE + e / NI;
+    if (a >= slab || a <= slab - PD) return false;
+  }
+  return true;
+}
 
 template <class T, bool A_K, bool B_K, class Epi, int GRP = kDense>
 __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) gemm_kernel(const GemmArgs g, const typename Epi::Params ep) {
@@ -658,10 +691,21 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   auto no_load = [](int) {};
 
   // prologue, in this issue order: A0 B0 A1 B1 A2
-  // epilogue reads in flight: slab 0's during the last stage, then up to
-  // PD slabs ahead (the main loop's fragment registers are free by then)
+  // Epilogue reads (an epilogue's per-slab global inputs, PD slabs in
+  // registers): slabs 0 .. PRE-1 are requested during the last two k-stages,
+  // one item per MFMA slot, and slab s + PRE one item at a time while slab s
+  // is processed.  Issued in bursts instead (all of a slab's loads at once),
+  // they had stalled each wave at the issue point with no other work beside
+  // it (~1 us per 16 loads); between the MFMAs of the last stages they are
+  // largely hidden.
   constexpr int PD = Epi::kPrefetchDepth < T::FM ? Epi::kPrefetchDepth : T::FM;
   static_assert(PD >= 1, "prefetch depth");
+  constexpr int PRE = PD > 1 ? PD - 1 : 1;
+  constexpr int NI = T::SLAB_ROWS * (T::BN / 8) / T::THREADS;  // items per thread and slab
+  // PRE_PER_STEP items in each of the 2 * KS steps of the last two stages;
+  // the stage before the last issues items [0, PRE_HALF)
+  constexpr int PRE_LOADS = PRE * NI, PRE_PER_STEP = (PRE_LOADS + 2 * KS - 1) / (2 * KS);
+  constexpr int PRE_HALF = KS * PRE_PER_STEP;
   typename Epi::template Prefetch<T> pf[PD];
   Frags<T> f[2];
   MnOff<T> mo;
@@ -704,9 +748,18 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   // each of them had cost issue slots the MFMA pipe waited on).  sa, sb: the
   // ring slots of A(kt) and B(kt), kt % 3 and kt % 2, compile-time constants
   // in the unrolled steady state (so no slot arithmetic runs between the
-  // MFMAs) and plain ints elsewhere.
-  auto stage = [&](int kt, auto lda, auto ldb, auto sa, auto sb) {
+  // MFMAs) and plain ints elsewhere.  TAIL: 1 for the stage before the last,
+  // 2 for the last; their MFMA slots carry the epilogue's first reads
+  // (pre_item below; read idx is item idx % NI of slab idx / NI).
+  auto pre_item = [&](int idx) {
+    if (idx < PRE_LOADS)
+      Epi::template prefetch_item<T>(ep, SlabCtx<T>{nullptr, r0, tn, idx / NI, m_end, g.N, goff}, pf[idx / NI], tid,
+                                     idx % NI);
+  };
+  auto stage = [&](int kt, auto lda, auto ldb, auto sa, auto sb, auto tail) {
     constexpr bool LDA = decltype(lda)::value, LDB = decltype(ldb)::value;
+    constexpr int TAIL = decltype(tail)::value;
+    static_assert(!(TAIL && (LDA || LDB)), "the last two stages load no operands");
     const int a0 = sa, b0 = sb;
     const int a1 = a0 == 2 ? 0 : a0 + 1, a2 = a0 == 0 ? 2 : a0 - 1;  // slots of A(kt+1), A(kt+2)
     const int b1 = b0 ^ 1;                                            // slot of B(kt+1); B(kt+2) reuses b0
@@ -714,65 +767,88 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
     const SWG_LDS char* bs = b_buf(b0);
     // LDB holds exactly when kt + 2 < nk: then this is not one of the last
     // two stages
-    const bool last = LDB ? false : kt + 1 == nk;
     const bool next = LDB ? true : kt + 1 < nk;
-    // the epilogue's first global reads go out under the last stage's MFMAs
-    if (last) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, r0, tn, 0, m_end, g.N, goff}, pf[0], tid);
+    constexpr int PL = TAIL ? PRE_PER_STEP : 0;
+    constexpr int P0 = TAIL == 2 ? PRE_HALF : 0;  // this stage's first epilogue read
     // steps 0 and 1: A(kt+2), half in each (A(2) came with the prologue)
     const i32x4 rA = rs_a(kt + 2);
-    step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[0], f[1], 1, acc, wm, wn, lane, mo, [&](int i) {
+    step<T, A_K, B_K, LDA ? LA / 2 : PL>(as, bs, f[0], f[1], 1, acc, wm, wn, lane, mo, [&](int i) {
       if constexpr (LDA) load_a_to(rA, kt + 2, a2, i);
+      if constexpr (TAIL) pre_item(P0 + i);
     });
-    step<T, A_K, B_K, LDA ? LA / 2 : 0>(as, bs, f[1], f[0], 2, acc, wm, wn, lane, mo, [&](int i) {
+    step<T, A_K, B_K, LDA ? LA / 2 : PL>(as, bs, f[1], f[0], 2, acc, wm, wn, lane, mo, [&](int i) {
       if constexpr (LDA) load_a_to(rA, kt + 2, a2, LA / 2 + i);
+      if constexpr (TAIL) pre_item(P0 + PL + i);
     });
-    step<T, A_K, B_K, 0>(as, bs, f[0], f[1], 3, acc, wm, wn, lane, mo, no_load);
+    step<T, A_K, B_K, PL>(as, bs, f[0], f[1], 3, acc, wm, wn, lane, mo, [&](int i) {
+      if constexpr (TAIL) pre_item(P0 + 2 * PL + i);
+    });
     // step 3: barrier, then the next stage's first fragments and B(kt+2)
     const SWG_LDS char* nas = as;
     const SWG_LDS char* nbs = bs;
     if (next) {
       // A(kt+1) and B(kt+1) must have landed; A(kt+2), issued after them,
-      // may stay in flight
+      // may stay in flight, and so may the epilogue reads of the stage before
+      // the last (issued after every operand load)
       if (LDB) wait_vmcnt<LA>();
-      else wait_vmcnt<0>();
+      else wait_vmcnt<TAIL == 1 ? 3 * PRE_PER_STEP * Epi::kLoadsPerItem : 0>();
       barrier();
       nas = a_buf(a1);
       nbs = b_buf(b1);
     }
     const i32x4 rB = rs_b(kt + 2);
-    step<T, A_K, B_K, LDB ? LB : 0>(nas, nbs, f[1], f[0], 0, acc, wm, wn, lane, mo, [&](int i) {
+    step<T, A_K, B_K, LDB ? LB : PL>(nas, nbs, f[1], f[0], 0, acc, wm, wn, lane, mo, [&](int i) {
       if constexpr (LDB) load_b_to(rB, kt + 2, b0, i);
+      if constexpr (TAIL) pre_item(P0 + 3 * PL + i);
     });
   };
   typedef integral_c<true> yes;
   typedef integral_c<false> no;
   int kt = 0;
-  if (nk > 2) stage(kt++, no{}, yes{}, int_c<0>{}, int_c<0>{});  // stage 0: A(2) came with the prologue
+  if (nk > 2) stage(kt++, no{}, yes{}, int_c<0>{}, int_c<0>{}, int_c<0>{});  // stage 0: A(2) came with the prologue
   // from kt = 1 on, six stages per trip: kt % 3 and kt % 2 run through
   // (1,1) (2,0) (0,1) (1,0) (2,1) (0,0)
   for (; kt + 7 < nk; kt += 6) {
-    stage(kt, yes{}, yes{}, int_c<1>{}, int_c<1>{});
-    stage(kt + 1, yes{}, yes{}, int_c<2>{}, int_c<0>{});
-    stage(kt + 2, yes{}, yes{}, int_c<0>{}, int_c<1>{});
-    stage(kt + 3, yes{}, yes{}, int_c<1>{}, int_c<0>{});
-    stage(kt + 4, yes{}, yes{}, int_c<2>{}, int_c<1>{});
-    stage(kt + 5, yes{}, yes{}, int_c<0>{}, int_c<0>{});
+    stage(kt, yes{}, yes{}, int_c<1>{}, int_c<1>{}, int_c<0>{});
+    stage(kt + 1, yes{}, yes{}, int_c<2>{}, int_c<0>{}, int_c<0>{});
+    stage(kt + 2, yes{}, yes{}, int_c<0>{}, int_c<1>{}, int_c<0>{});
+    stage(kt + 3, yes{}, yes{}, int_c<1>{}, int_c<0>{}, int_c<0>{});
+    stage(kt + 4, yes{}, yes{}, int_c<2>{}, int_c<1>{}, int_c<0>{});
+    stage(kt + 5, yes{}, yes{}, int_c<0>{}, int_c<0>{}, int_c<0>{});
   }
-  for (; kt + 2 < nk; ++kt) stage(kt, yes{}, yes{}, kt % 3, kt & 1);
-  for (; kt < nk; ++kt) stage(kt, no{}, no{}, kt % 3, kt & 1);  // the last two stages load nothing
+  for (; kt + 2 < nk; ++kt) stage(kt, yes{}, yes{}, kt % 3, kt & 1, int_c<0>{});
+  // The last two stages load no operands and request slabs 0 .. PRE-1 (with
+  // fewer than two stages, the missing stages' reads are issued at once).
+  if (kt + 1 < nk) {
+    stage(kt, no{}, no{}, kt % 3, kt & 1, int_c<1>{});
+    ++kt;
+  } else {
+#pragma unroll
+    for (int i = 0; i < PRE_HALF; ++i) pre_item(i);
+  }
+  if (kt < nk) {
+    stage(kt, no{}, no{}, kt % 3, kt & 1, int_c<2>{});
+    ++kt;
+  } else {
+#pragma unroll
+    for (int i = PRE_HALF; i < 2 * PRE_HALF; ++i) pre_item(i);
+  }
   // Every stage load has been waited for.  The only vector memory reads in
   // flight now are the epilogue prefetches, which must stay in flight: the
   // barriers below are bare s_barriers, not __syncthreads() (whose fence
   // would wait for them).
-  if (nk == 0) Epi::template prefetch<T>(ep, SlabCtx<T>{nullptr, r0, tn, 0, m_end, g.N, goff}, pf[0], tid);
   barrier();
 
   // ---- epilogue: one 32-row slab per wave row at a time through LDS; the
-  // global reads of slab s+PD-1 are issued before slab s is processed ----
+  // global reads of slabs PRE .. FM-1 are spread evenly over the processing
+  // of slabs 0 .. FM-2, one or so per item ----
+  constexpr int EPI_READS = PD > 1 ? (T::FM - PRE) * NI : 0;
+  constexpr int APPLIES = T::FM > 1 ? T::FM - 1 : 1;
+  auto epi_lo = [](int s) { return (EPI_READS * s + APPLIES - 1) / APPLIES; };
+  static_assert(epi_schedule_ok<EPI_READS, APPLIES, NI, PRE, PD>(),
+                "every slab's reads are issued before it is processed, into registers already consumed");
   SWG_LDS float* slab = (SWG_LDS float*)smem;
   SlabCtx<T> ctx{slab, r0, tn, 0, m_end, g.N, goff};
-#pragma unroll
-  for (int s = 1; s + 1 < PD; ++s) Epi::template prefetch<T>(ep, SlabCtx<T>{slab, r0, tn, s, m_end, g.N, goff}, pf[s], tid);
 #pragma unroll
   for (int s = 0; s < T::FM; ++s) {
     ctx.s = s;
@@ -786,11 +862,19 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
         f32x4 v = {acc[s][j][4 * q + 0], acc[s][j][4 * q + 1], acc[s][j][4 * q + 2], acc[s][j][4 * q + 3]};
         *(SWG_LDS f32x4*)(slab + sr * T::SLAB_LD + c) = v;
       }
-    // after the accumulator writes, whose staging registers are then free
-    if (s + PD - 1 < T::FM && PD > 1)
-      Epi::template prefetch<T>(ep, SlabCtx<T>{slab, r0, tn, s + PD - 1, m_end, g.N, goff}, pf[(s + PD - 1) % PD], tid);
     barrier();
-    Epi::template apply<T>(ep, ctx, pf[s % PD], tid);
+    Epi::template apply<T>(ep, ctx, pf[s % PD], tid, [&](int k) {
+      // apply(s) issues epilogue reads [epi_lo(s), epi_lo(s + 1)), item k
+      // its share; read e is item e % NI of slab PRE + e / NI
+      const int a = epi_lo(s), cnt = epi_lo(s + 1) - a;
+#pragma unroll
+      for (int u = 0; u < (EPI_READS + APPLIES * NI - 1) / (APPLIES * NI) + 1; ++u) {
+        const int e = a + (k * cnt + NI - 1) / NI + u;
+        if (e < EPI_READS && e < a + ((k + 1) * cnt + NI - 1) / NI)
+          Epi::template prefetch_item<T>(ep, SlabCtx<T>{slab, r0, tn, PRE + e / NI, m_end, g.N, goff},
+                                         pf[(PRE + e / NI) % PD], tid, e % NI);
+      }
+    });
   }
 }
 
@@ -798,7 +882,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
 // Plain epilogue: C = bf16(acc), row-major with leading dimension ldc.
 // ---------------------------------------------------------------------------
 struct EpiStore {
-  static constexpr int kPrefetchDepth = 1;
+  static constexpr int kPrefetchDepth = 1, kLoadsPerItem = 0;
   struct Params {
     uint16_t* C;
     int64_t ldc;
@@ -806,9 +890,9 @@ struct EpiStore {
   template <class T>
   struct Prefetch {};
   template <class T>
-  __device__ static void prefetch(const Params&, const SlabCtx<T>&, Prefetch<T>&, int) {}
-  template <class T>
-  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>&, int tid) {
+  __device__ static void prefetch_item(const Params&, const SlabCtx<T>&, Prefetch<T>&, int, int) {}
+  template <class T, class Hook>
+  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>&, int tid, Hook&& hook) {
     constexpr int CPR = T::BN / 8;  // 8-column chunks per slab row
     constexpr int ITEMS = T::SLAB_ROWS * CPR;
     static_assert(ITEMS % T::THREADS == 0, "slab items must split evenly");
@@ -816,6 +900,7 @@ struct EpiStore {
     const int ldc = (int)p.ldc;
 #pragma unroll
     for (int k = 0; k < ITEMS / T::THREADS; ++k) {
+      hook(k);  // this item's share of a later slab's reads, ahead of its stores
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
       const int col = c.tn * T::BN + ch * 8;
@@ -831,21 +916,22 @@ struct EpiStore {
 // pitch BN.  The split-tail reduce kernel adds a tile's parts in order.
 // ---------------------------------------------------------------------------
 struct EpiPartial {
-  static constexpr int kPrefetchDepth = 1;
+  static constexpr int kPrefetchDepth = 1, kLoadsPerItem = 0;
   struct Params {
     float* P;
   };
   template <class T>
   struct Prefetch {};
   template <class T>
-  __device__ static void prefetch(const Params&, const SlabCtx<T>&, Prefetch<T>&, int) {}
-  template <class T>
-  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>&, int tid) {
+  __device__ static void prefetch_item(const Params&, const SlabCtx<T>&, Prefetch<T>&, int, int) {}
+  template <class T, class Hook>
+  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>&, int tid, Hook&& hook) {
     constexpr int CPR = T::BN / 8;
     constexpr int ITEMS = T::SLAB_ROWS * CPR;
     static_assert(ITEMS % T::THREADS == 0, "slab items must split evenly");
 #pragma unroll
     for (int k = 0; k < ITEMS / T::THREADS; ++k) {
+      hook(k);  // this item's share of a later slab's reads, ahead of its stores
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
       const f32x8 v = c.read8(sr, ch * 8);
@@ -894,7 +980,7 @@ struct EpiStoreResidual {
   // every slab's residual is requested before the first slab is stored:
   // measured 0.04 ms over both residual GEMMs of the 11136x3584x14336 block
   // against 0.11 ms at two slabs ahead
-  static constexpr int kPrefetchDepth = 4;
+  static constexpr int kPrefetchDepth = 4, kLoadsPerItem = 1;
   struct Params {
     uint16_t* C;
     int64_t ldc;
@@ -907,26 +993,24 @@ struct EpiStoreResidual {
     u32x4 r[N];
   };
   template <class T>
-  __device__ static void prefetch(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
+  __device__ static void prefetch_item(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid, int k) {
     constexpr int CPR = T::BN / 8;
     const brsrc_t src = rows_rsrc(p.R + (int64_t)c.r0 * p.ldr, (int64_t)(c.M - c.r0) * p.ldr * 2);
     const int ldr = (int)p.ldr;
-#pragma unroll
-    for (int k = 0; k < Prefetch<T>::N; ++k) {
-      const int it = tid + k * T::THREADS;
-      const int sr = it / CPR, ch = it % CPR;
-      const int col = c.tn * T::BN + ch * 8;
-      const uint32_t off = col < c.N ? (uint32_t)((c.row(sr) - c.r0) * ldr + col) * 2u : kOffOutOfRange;
-      pf.r[k] = bload16(src, off);
-    }
+    const int it = tid + k * T::THREADS;
+    const int sr = it / CPR, ch = it % CPR;
+    const int col = c.tn * T::BN + ch * 8;
+    const uint32_t off = col < c.N ? (uint32_t)((c.row(sr) - c.r0) * ldr + col) * 2u : kOffOutOfRange;
+    pf.r[k] = bload16(src, off);
   }
-  template <class T>
-  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
+  template <class T, class Hook>
+  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid, Hook&& hook) {
     constexpr int CPR = T::BN / 8;
     const brsrc_t dst = rows_rsrc(p.C + (int64_t)c.r0 * p.ldc, (int64_t)(c.M - c.r0) * p.ldc * 2);
     const int ldc = (int)p.ldc;
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
+      hook(k);  // this item's share of a later slab's reads, ahead of its stores
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
       const int col = c.tn * T::BN + ch * 8;

@@ -32,7 +32,7 @@ namespace swg {
 // preact halves and h = rn(left * silu(gate)) from the rounded values.
 // ---------------------------------------------------------------------------
 struct EpiSwigluFwd {
-  static constexpr int kPrefetchDepth = 1;
+  static constexpr int kPrefetchDepth = 1, kLoadsPerItem = 0;
   struct Params {
     uint16_t* preact;  // [M, 2I]
     uint16_t* h;       // [M, I]
@@ -41,9 +41,9 @@ struct EpiSwigluFwd {
   template <class T>
   struct Prefetch {};
   template <class T>
-  __device__ static void prefetch(const Params&, const SlabCtx<T>&, Prefetch<T>&, int) {}
-  template <class T>
-  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>&, int tid) {
+  __device__ static void prefetch_item(const Params&, const SlabCtx<T>&, Prefetch<T>&, int, int) {}
+  template <class T, class Hook>
+  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>&, int tid, Hook&& hook) {
     constexpr int HALF = T::BN / 2;
     constexpr int CPR = HALF / 8;
     constexpr int ITEMS = T::SLAB_ROWS * CPR;
@@ -54,6 +54,7 @@ struct EpiSwigluFwd {
     const brsrc_t hdst = rows_rsrc(p.h + (int64_t)c.r0 * p.I, rows * 2 * p.I);
 #pragma unroll
     for (int k = 0; k < ITEMS / T::THREADS; ++k) {
+      hook(k);  // this item's share of a later slab's reads, ahead of its stores
       const int it = tid + k * T::THREADS;
       const int sr = it / CPR, ch = it % CPR;
       const int rl = c.row(sr) - c.r0;
@@ -89,7 +90,7 @@ template <bool STORE_H>
 struct EpiSwigluBwdT {
   // three slabs of preact reads in flight: the epilogue waits on their
   // latency otherwise
-  static constexpr int kPrefetchDepth = 3;
+  static constexpr int kPrefetchDepth = 3, kLoadsPerItem = 2;
   struct Params {
     const uint16_t* preact;  // [M, 2I]
     uint16_t* grad_preact;   // [M, 2I]
@@ -102,37 +103,34 @@ struct EpiSwigluBwdT {
     u32x4 left[N], gate[N];
   };
   // Addresses are 32-bit byte offsets from the tile's first row: a tile
-  // spans BM rows of at most 2^21 elements, well inside 2^31 bytes, and the
-  // per-item registers stay 32-bit.
+  // spans BM rows of at most 2^21 elements, well inside 2^31 bytes.  Item
+  // k's row is q + item_row(k) (SlabCtx), so its offset is a per-thread base
+  // plus item_row(k) times the row pitch, a scalar product.
   template <class T>
-  __device__ static void prefetch(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
-    constexpr int CPR = T::BN / 8;
-    const int I = (int)p.I;
+  __device__ static void prefetch_item(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid, int k) {
+    constexpr int CPR = SlabCtx<T>::CPR;
+    const uint32_t pitch = (uint32_t)p.I * 4u;  // bytes per preact row
     const brsrc_t src = rows_rsrc(p.preact + (int64_t)c.r0 * 2 * p.I, (int64_t)(c.M - c.r0) * 4 * p.I);
-#pragma unroll
-    for (int k = 0; k < Prefetch<T>::N; ++k) {
-      const int it = tid + k * T::THREADS;
-      const int sr = it / CPR, ch = it % CPR;
-      const int rl = c.row(sr) - c.r0;
-      const uint32_t off = (uint32_t)(rl * 2 * I + c.tn * T::BN + ch * 8) * 2u;
-      pf.left[k] = bload16(src, off);
-      pf.gate[k] = bload16(src, off + (uint32_t)I * 2u);
-    }
+    const int q = tid / CPR, ch = tid % CPR;
+    const uint32_t off = (uint32_t)q * pitch + (uint32_t)(c.tn * T::BN + ch * 8) * 2u + (uint32_t)c.item_row(k) * pitch;
+    pf.left[k] = bload16(src, off);
+    pf.gate[k] = bload16(src, off + pitch / 2u);
   }
-  template <class T>
-  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid) {
-    constexpr int CPR = T::BN / 8;
-    const int I = (int)p.I;
+  template <class T, class Hook>
+  __device__ static void apply(const Params& p, const SlabCtx<T>& c, Prefetch<T>& pf, int tid, Hook&& hook) {
+    constexpr int CPR = SlabCtx<T>::CPR, P = SlabCtx<T>::P;
+    const uint32_t gpitch = (uint32_t)p.I * 4u, hpitch = (uint32_t)p.I * 2u;  // bytes per row
     const int64_t rows = c.M - c.r0;
     const brsrc_t gdst = rows_rsrc(p.grad_preact + (int64_t)c.r0 * 2 * p.I, rows * 4 * p.I);
     const brsrc_t hdst = rows_rsrc(STORE_H ? p.h + (int64_t)c.r0 * p.I : nullptr, STORE_H ? rows * 2 * p.I : 0);
+    const int q = tid / CPR, ch = tid % CPR;
+    const uint32_t col2 = (uint32_t)(c.tn * T::BN + ch * 8) * 2u;
+    const uint32_t gbase = (uint32_t)q * gpitch + col2, hbase = (uint32_t)q * hpitch + col2;
 #pragma unroll
     for (int k = 0; k < Prefetch<T>::N; ++k) {
-      const int it = tid + k * T::THREADS;
-      const int sr = it / CPR, ch = it % CPR;
-      const int rl = c.row(sr) - c.r0;
-      const int col = c.tn * T::BN + ch * 8;
-      const f32x8 dout = c.read8(sr, ch * 8);
+      hook(k);  // this item's share of a later slab's reads, ahead of its stores
+      const uint32_t r = (uint32_t)c.item_row(k);
+      const f32x8 dout = c.read8(q + k * P, ch * 8);
       const f32x8 left = unpack8(pf.left[k]), gate = unpack8(pf.gate[k]);
       f32x8 dl, dg, h;
 #pragma unroll
@@ -142,11 +140,11 @@ struct EpiSwigluBwdT {
         dg[e] = (dout[e] * left[e]) * a.dsilu;
         h[e] = left[e] * a.silu;
       }
-      const uint32_t off = (uint32_t)(rl * 2 * I + col) * 2u;
+      const uint32_t off = gbase + r * gpitch;
       // streaming stores: nothing in this kernel reads them back
       bstore16(gdst, off, pack8(dl));
-      bstore16(gdst, off + (uint32_t)I * 2u, pack8(dg));
-      if constexpr (STORE_H) bstore16(hdst, (uint32_t)(rl * I + col) * 2u, pack8(h));
+      bstore16(gdst, off + hpitch, pack8(dg));
+      if constexpr (STORE_H) bstore16(hdst, hbase + r * hpitch, pack8(h));
     }
   }
 };
