@@ -887,6 +887,8 @@ struct EpiStore {
     uint16_t* C;
     int64_t ldc;
   };
+  // the same store for output columns n..
+  static Params cols_from(const Params& p, int64_t n) { return {p.C + n, p.ldc}; }
   template <class T>
   struct Prefetch {};
   template <class T>

@@ -97,6 +97,10 @@ struct EpiSwigluBwdT {
     uint16_t* h;             // [M, I]
     int64_t I;
   };
+  // the same epilogue for output columns n.. (left, gate and h move by n)
+  static Params cols_from(const Params& p, int64_t n) {
+    return {p.preact + n, p.grad_preact + n, p.h != nullptr ? p.h + n : nullptr, p.I};
+  }
   template <class T>
   struct Prefetch {
     static constexpr int N = T::SLAB_ROWS * (T::BN / 8) / T::THREADS;
@@ -383,18 +387,70 @@ KkTile pick_kk_tile(int64_t M, int64_t N, int cus) {
   return best;
 }
 
-// A K-major x K-major GEMM (the dout GEMM and its plain-store twin) in the
-// tile shape pick_kk_tile chooses.
+// The cost of one launch in the model above, in units of one round of
+// 256 x 256 tiles; -1 when the shape does not divide N.
+double kk_cost(int64_t M, int64_t N, KkTile k, int64_t C) {
+  static const int bm[] = {256, 256, 128, 128}, bn[] = {256, 128, 256, 128};
+  static const double rate[] = {1.0, 0.945, 0.903, 0.723};
+  if (k > kTileMid || N <= 0 || N % bn[k] != 0) return -1.0;
+  const int64_t tiles = ((M + bm[k] - 1) / bm[k]) * (N / bn[k]);
+  const int64_t full = tiles / C, rem = tiles % C;
+  const double rounds = (double)full + (rem > 0 ? 0.5 + 0.5 * (double)rem / (double)C : 0.0);
+  return rounds * bm[k] * bn[k] / rate[k] / 65536.0;
+}
+
+// A launch plan for the dout GEMM: one launch in the shape pick_kk_tile
+// chooses, or 256 x 256 tiles over the first n1 columns and another shape
+// over the rest, when that fills the rounds better by the same model (a
+// second launch counted as 0.02 of a round).  At 8192 x 11008 the 1376 tiles
+// of 256 x 256 run 5.4 rounds; 1280 of them (40 tile columns) fill 5 and the
+// last 768 columns run as 192 tiles of 256 x 128.
+struct KkPlan {
+  KkTile first;
+  int64_t n1;  // columns of the first launch (N: one launch)
+  KkTile second;
+};
+KkPlan plan_kk(int64_t M, int64_t N, int cus) {
+  const KkTile one = pick_kk_tile(M, N, cus);
+  KkPlan best{one, N, one};
+  if (one == kTileSmall || cus <= 0) return best;
+  double best_cost = kk_cost(M, N, one, cus);
+  for (int64_t n1 = 256; n1 < N; n1 += 256) {
+    const double c1 = kk_cost(M, n1, kTileBig, cus);
+    for (int k = kTileBig; k <= kTileMid; ++k) {
+      const double c2 = kk_cost(M, N - n1, (KkTile)k, cus);
+      if (c1 < 0 || c2 < 0) continue;
+      if (c1 + c2 + 0.02 < best_cost - 1e-9) {
+        best = {kTileBig, n1, (KkTile)k};
+        best_cost = c1 + c2 + 0.02;
+      }
+    }
+  }
+  return best;
+}
+
 template <class Epi>
-int run_gemm_kk(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
-                const typename Epi::Params& ep, hipStream_t st) {
-  switch (pick_kk_tile(M, N, device_compute_units())) {
+int run_gemm_kk_one(KkTile k, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N,
+                    int64_t K, const typename Epi::Params& ep, hipStream_t st) {
+  switch (k) {
     case kTileBig: return run_gemm<TBig, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
     case kTileWide: return run_gemm<TWide, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
     case kTileTall: return run_gemm<TTall, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
     case kTileMid: return run_gemm<TMid, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
     default: return run_gemm<TSmall, true, true, Epi>(A, lda, B, ldb, M, N, K, 0, ep, st);
   }
+}
+
+// A K-major x K-major GEMM (the dout GEMM and its plain-store twin) by
+// plan_kk: the second launch covers columns [n1, N), B's rows and the
+// epilogue's column base moved by n1 (Epi::cols_from).
+template <class Epi>
+int run_gemm_kk(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                const typename Epi::Params& ep, hipStream_t st) {
+  const KkPlan pl = plan_kk(M, N, device_compute_units());
+  int s = run_gemm_kk_one<Epi>(pl.first, A, lda, B, ldb, M, pl.n1, K, ep, st);
+  if (s != SWIGLU_OK || pl.n1 == N) return s;
+  return run_gemm_kk_one<Epi>(pl.second, A, lda, B + pl.n1 * ldb, ldb, M, N - pl.n1, K, Epi::cols_from(ep, pl.n1), st);
 }
 
 struct Scratch {

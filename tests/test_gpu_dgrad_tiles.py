@@ -4,7 +4,9 @@ The fused dgrad (dout = dy . W_down^T with the SwiGLU backward in its
 epilogue; the note "SwiGLU MLP forward principle, backward chain and
 optimisation", sections 2-4), its save-h twin and its plain-store twin take
 256x256, 256x128, 128x256 or 128x128 tiles by the launch's estimated rounds
-on the GPU.  These shapes select each of them (and ragged token counts):
+on the GPU, or 256x256 tiles over the first columns and another shape over
+the rest in a second launch when that fills the rounds better.  These shapes
+select each of them (and ragged token counts):
 the outputs are checked against the fp64 oracle (per-tensor bound; h within
 2 bf16 ulp) and bit for bit against the grouped launch with one expert,
 which keeps its own tile rule: the tile shape does not change any element's
@@ -26,7 +28,9 @@ pytestmark = pytest.mark.gpu
 SHAPES = [
     ((640, 7680, 512), "128x256"),
     ((2048, 2816, 1024), "256x128"),
-    ((3333, 6016, 512), "256x128, ragged M"),
+    # 14 x 24 tiles of 256 x 256 would fill 1.3 rounds: 256 x 256 over the
+    # first 4608 columns and 256 x 128 over the last 1408, two launches
+    ((3333, 6016, 512), "256x256 + 256x128 split, ragged M"),
     ((2148, 5120, 768), "256x256"),
     ((700, 1024, 1024), "128x128"),
 ]
