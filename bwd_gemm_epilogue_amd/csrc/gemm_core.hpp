@@ -706,6 +706,9 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   // the stage before the last issues items [0, PRE_HALF)
   constexpr int PRE_LOADS = PRE * NI, PRE_PER_STEP = (PRE_LOADS + 2 * KS - 1) / (2 * KS);
   constexpr int PRE_HALF = KS * PRE_PER_STEP;
+  // epilogue loads the stage before the last issues ahead of its wait (steps
+  // 1-3; items past PRE_LOADS are skipped)
+  constexpr int TAIL1_LOADS = (3 * PRE_PER_STEP < PRE_LOADS ? 3 * PRE_PER_STEP : PRE_LOADS) * Epi::kLoadsPerItem;
   typename Epi::template Prefetch<T> pf[PD];
   Frags<T> f[2];
   MnOff<T> mo;
@@ -791,7 +794,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
       // may stay in flight, and so may the epilogue reads of the stage before
       // the last (issued after every operand load)
       if (LDB) wait_vmcnt<LA>();
-      else wait_vmcnt<TAIL == 1 ? 3 * PRE_PER_STEP * Epi::kLoadsPerItem : 0>();
+      else wait_vmcnt<TAIL == 1 ? TAIL1_LOADS : 0>();
       barrier();
       nas = a_buf(a1);
       nbs = b_buf(b1);
