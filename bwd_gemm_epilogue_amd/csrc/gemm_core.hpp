@@ -203,16 +203,18 @@ __device__ __forceinline__ void bstore16(brsrc_t r, uint32_t off, u32x4 v) {
 }
 
 // One wave-wide direct-to-LDS load: lane i's 16 B at byte offset
-// vbase + sadd of the buffer land at LDS address dst + 16*i.  Issued as
+// voff + soff of the buffer land at LDS address m0 + 16*i.  Issued as
 // inline asm so that the compiler's wait-count pass does not track these LDS
 // writes: it cannot tell the ring stages apart and would otherwise wait for
 // every in-flight stage before each LDS read.  Ordering is explicit instead
-// (wait_vmcnt + barrier in the main loop).  The offset is summed inside the
-// asm so that the compiler keeps one per-lane base per swizzle class instead
-// of hoisting one VGPR per 1 KB block out of the K loop.  M0 holds the LDS
-// base; the v_add between writing M0 and the LDS DMA that reads it is the
-// one wait state the hardware needs there (an s_nop before cost one more
-// issue slot per load).  M0 is a reserved register, which clang does not
+// (wait_vmcnt + barrier in the main loop).  voff: a per-lane offset held in a
+// VGPR for the whole K loop (one per 1 KB block), which alone decides the
+// range check; soff: a scalar added after it (the hardware leaves the scalar
+// offset out of the range check), here a K-major stage's k offset.  Summing
+// the two with a v_add before each load had cost a VALU issue slot per load
+// between the MFMAs (~1% on every GEMM).  M0 holds the LDS base; the s_nop
+// is the one wait state the hardware needs between writing M0 and the LDS
+// DMA that reads it.  M0 is a reserved register, which clang does not
 // accept in a clobber list (it warns that it may not be preserved), so it is
 // written here without one.  That is safe because nothing else in these
 // kernels reads M0: in the compiled library every M0 write is one of these
@@ -222,14 +224,13 @@ __device__ __forceinline__ void bstore16(brsrc_t r, uint32_t off, u32x4 v) {
 // m0: the LDS byte address of the 1 KB destination, a scalar (computed from
 // a hoisted LDS base with scalar arithmetic: a pointer-derived value had been
 // built in VGPRs and moved back with v_readfirstlane for every load).
-__device__ __forceinline__ void dma16(const i32x4& rsrc, int m0, uint32_t vbase, uint32_t sadd) {
-  uint32_t voff;
+__device__ __forceinline__ void dma16(const i32x4& rsrc, int m0, uint32_t voff, uint32_t soff) {
   asm volatile(
-      "s_mov_b32 m0, %3\n\t"
-      "v_add_u32 %0, %1, %2\n\t"
-      "buffer_load_dwordx4 %0, %4, 0 offen lds"
-      : "=&v"(voff)
-      : "v"(vbase), "s"(sadd), "s"(m0), "s"(rsrc)
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %3, %1 offen lds"
+      :
+      : "v"(voff), "s"(soff), "s"(m0), "s"(rsrc)
       : "memory");
 }
 
@@ -652,34 +653,33 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   // load block idx of stage j into ring slot s (s = j % 3 for A, j % 2 for B)
   // LDS byte address of this wave's first 1 KB block in the ring, a scalar
   const int lds_wave = __builtin_amdgcn_readfirstlane((int)(uintptr_t)smem) + wave * 1024;
-  // An MN-major operand's block offsets do not change from stage to stage
-  // (its descriptor moves instead), so they are folded into per-block lane
-  // offsets held in VGPRs: as 2 x 8 loop-invariant SGPRs they had pushed the
-  // unrolled loop into SGPR spills (v_readlane reloads every stage).
+  // Each 1 KB block's offset within the operand's rows is folded into a
+  // per-block lane offset held in a VGPR for the whole K loop (an MN-major
+  // operand's descriptor moves from stage to stage instead; a K-major one's
+  // k offset goes in the DMA's scalar offset).  As 2 x 8 loop-invariant
+  // SGPRs they had pushed the unrolled loop into SGPR spills (v_readlane
+  // reloads every stage).
   uint32_t vma[LA], vmb[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    vma[i] = A_K ? 0u : ((i & 1) ? va1 : va0) + dma_block_add<T::BM, false>(g.lda, wave + i * T::WAVES, 0);
-    if constexpr (!A_K) asm volatile("" : "+v"(vma[i]));
+    vma[i] = ((i & 1) ? va1 : va0) + dma_block_add<T::BM, A_K>(g.lda, wave + i * T::WAVES, 0);
+    asm volatile("" : "+v"(vma[i]));
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    vmb[i] = B_K ? 0u : ((i & 1) ? vb1 : vb0) + dma_block_add<T::BN, false>(g.ldb, wave + i * T::WAVES, 0);
-    if constexpr (!B_K) asm volatile("" : "+v"(vmb[i]));
+    vmb[i] = ((i & 1) ? vb1 : vb0) + dma_block_add<T::BN, B_K>(g.ldb, wave + i * T::WAVES, 0);
+    asm volatile("" : "+v"(vmb[i]));
   }
+  // a K-major stage's k offset, 2 * j * BK bytes (within every row, K being
+  // a multiple of BK), goes in the scalar offset; the row range check is
+  // decided by the per-lane offsets
   auto load_a_to = [&](const i32x4& r, int j, int s, int idx) {
     const int m0 = lds_wave + s * T::A_BYTES + idx * T::WAVES * 1024;
-    if constexpr (A_K)
-      dma16(r, m0, (idx & 1) ? va1 : va0, dma_block_add<T::BM, true>(g.lda, wave + idx * T::WAVES, j * T::BK));
-    else
-      dma16(r, m0, vma[idx], 0u);
+    dma16(r, m0, vma[idx], A_K ? (uint32_t)(2 * j * T::BK) : 0u);
   };
   auto load_b_to = [&](const i32x4& r, int j, int s, int idx) {
     const int m0 = lds_wave + 3 * T::A_BYTES + s * T::B_BYTES + idx * T::WAVES * 1024;
-    if constexpr (B_K)
-      dma16(r, m0, (idx & 1) ? vb1 : vb0, dma_block_add<T::BN, true>(g.ldb, wave + idx * T::WAVES, j * T::BK));
-    else
-      dma16(r, m0, vmb[idx], 0u);
+    dma16(r, m0, vmb[idx], B_K ? (uint32_t)(2 * j * T::BK) : 0u);
   };
   auto load_a = [&](const i32x4& r, int j, int idx) { load_a_to(r, j, j % 3, idx); };
   auto load_b = [&](const i32x4& r, int j, int idx) { load_b_to(r, j, j & 1, idx); };
