@@ -275,7 +275,7 @@ def main():
             return 1
         return run
 
-    ab = save_h_ab = residual = None
+    ab = save_h_ab = residual = library_gemm = None
     if args.ab_pairs > 0:
         def seg_unfused():
             sw.swiglu_bwd_dgrad_plain(dy, Wd, dout)
@@ -285,6 +285,11 @@ def main():
             "fused": timed(lambda: sw.swiglu_bwd_dgrad_fused(dy, Wd, preact, gp, h_bwd)),
             "unfused": timed(seg_unfused),
             "fused_gp_only": timed(lambda: sw.swiglu_bwd_dgrad_fused_gp(dy, Wd, preact, gp)),
+            # context, not the product: this library's plain dgrad GEMM (U1)
+            # against the platform's library GEMM (torch.matmul, hipBLASLt)
+            # computing the same product dout = dy . W_down^T
+            "plain_gemm": timed(lambda: sw.swiglu_bwd_dgrad_plain(dy, Wd, dout)),
+            "torch_matmul": timed(lambda: torch.matmul(dy, Wd.t(), out=dout)),
         }
         if D == Dout:
             y_res = torch.empty((M, D), dtype=bf, device=dev)
@@ -302,6 +307,14 @@ def main():
         one = {n: [v[0] for v in smp[n]] for n in smp}
         ab = {"pairs": args.ab_pairs, **paired_summary(one["fused"], one["unfused"], "fused", "unfused"),
               "dout_hbm_bytes_avoided": 2 * M * I * 2}
+        lib = paired_summary(one["plain_gemm"], one["torch_matmul"], "plain_gemm", "torch_matmul")
+        fl_d = flops["bwd_dgrad_fused"]
+        library_gemm = {"pairs": args.ab_pairs, "what": "dout = dy . W_down^T, bf16 out, no epilogue",
+                        "plain_gemm_ms": lib["plain_gemm_ms_median"], "torch_matmul_ms": lib["torch_matmul_ms_median"],
+                        "paired_delta_plain_vs_torch": lib["paired_delta"],
+                        "plain_gemm_tflops": round(fl_d / (lib["plain_gemm_ms_median"] * 1e-3) / 1e12, 2),
+                        "torch_matmul_tflops": round(fl_d / (lib["torch_matmul_ms_median"] * 1e-3) / 1e12, 2),
+                        "fused_ms_same_rounds": round(float(np.median(one["fused"])), 4)}
         gp_only = paired_summary(one["fused_gp_only"], one["fused"], "gp_only", "fused")
         save_h_ab = {"pairs": args.ab_pairs,
                   "bwd_dgrad_gp_ms": gp_only["gp_only_ms_median"],
@@ -428,6 +441,7 @@ def main():
         "ab_fused_vs_unfused": ab,
         "save_h_variant": save_h_ab,
         "residual_block": residual,
+        "library_gemm_context": library_gemm,
         "block_drop_h_vs_save_h": block,
         "stack": stack,
         "roofline": roofline,
