@@ -387,24 +387,36 @@ __device__ __forceinline__ void step(const SWG_LDS char* As, const SWG_LDS char*
 
 // blockIdx -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
 // the 8 XCDs, so each XCD is first given a contiguous run of tile ids (its own
-// L2 then sees neighbouring tiles), and tile ids are walked in groups of
-// GROUP_M tile rows so that concurrently running tiles share A and B panels.
+// L2 then sees neighbouring tiles), and tile ids are walked in groups of GM
+// tile rows so that concurrently running tiles share A and B panels.  32
+// tiles of an XCD as 4 rows x 8 columns or 8 x 4 share the same 12 panels;
+// the wider form puts 8 neighbouring column tiles side by side, whose slices
+// of an MN-major B are one contiguous run per k-row.  Measured in randomly
+// interleaved rounds: GEMM-1 (MN-major B) 2.5% faster at the target shape
+// and 4.6% at the Llama-like one with GM = 4 than with 8, the dout GEMMs
+// ~1%, the dx GEMM 1.5%; dW1, whose A is MN-major along m, 0.8% slower.
+// group_rows<A_K>() is the rule: 4 unless A is MN-major.
 __device__ __forceinline__ int xcd_linear(int pid, int total) {
   const int per = total / 8, rem = total % 8;
   const int xcd = pid % 8, local = pid / 8;
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
+template <bool A_K>
+constexpr int group_rows() {
+  return A_K ? 4 : 8;
+}
+template <int GM>
 __device__ __forceinline__ void tile_order(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GROUP_M = 8;
-  const int group = id / (GROUP_M * tiles_n);
-  const int first_m = group * GROUP_M;
-  const int gsize = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
-  const int in_group = id - group * GROUP_M * tiles_n;
+  const int group = id / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int in_group = id - group * GM * tiles_n;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
 }
+template <int GM>
 __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  tile_order(xcd_linear(pid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+  tile_order<GM>(xcd_linear(pid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 // Token range [lo, hi) of group e, clamped into [0, M] and made non-empty
@@ -514,6 +526,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
+  constexpr int GM = group_rows<A_K>();
   // tile coordinates; r0 / m_end: the tile's first row and the row bound;
   // Ag, Bg, Kg: this tile's operands and reduction length
   int tm, tn, r0, m_end, Kg = g.K;
@@ -521,7 +534,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   const uint16_t* Bg = g.B;
   int64_t goff = 0;
   if constexpr (GRP == kDense) {
-    tile_order(xcd_linear(blockIdx.x, g.tile_count), g.tiles_m, g.tiles_n, tm, tn);
+    tile_order<GM>(xcd_linear(blockIdx.x, g.tile_count), g.tiles_m, g.tiles_n, tm, tn);
     r0 = tm * T::BM;
     m_end = g.M;
   } else if constexpr (GRP == kSplitTail) {
@@ -529,7 +542,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
     // [s * nst / splits, (s + 1) * nst / splits) and writes its fp32 partial
     // tile to slot t * splits + s of the epilogue's buffer
     const int t = blockIdx.x / g.splits, sp = blockIdx.x - t * g.splits;
-    tile_order(g.tile_base + t, g.tiles_m, g.tiles_n, tm, tn);
+    tile_order<GM>(g.tile_base + t, g.tiles_m, g.tiles_n, tm, tn);
     const int nst = (g.K + T::BK - 1) / T::BK;
     const int k0 = sp * nst / g.splits * T::BK;
     const int k1 = (sp + 1) * nst / g.splits * T::BK;
@@ -542,7 +555,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
   } else if constexpr (GRP == kGroupM) {
     static_assert(A_K, "grouped over M: A is the K-major token operand");
     int r, grp;
-    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, r, tn);
+    tile_coords<GM>(blockIdx.x, g.tiles_m, g.tiles_n, r, tn);
     // past the last tile row of the last group: the whole workgroup leaves
     // (the condition is uniform across it, before any barrier)
     if (!find_group_row<T::BM>(g.group_off, g.groups, g.M, r, grp, r0, m_end)) return;
@@ -559,7 +572,7 @@ __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu
     const int per = g.tiles_m * g.tiles_n;
     const int id = blockIdx.x;
     const int grp = id / per;
-    tile_order(id - grp * per, g.tiles_m, g.tiles_n, tm, tn);
+    tile_order<GM>(id - grp * per, g.tiles_m, g.tiles_n, tm, tn);
     int lo, hi;
     group_range(g.group_off, grp, g.K, lo, hi);
     lo = __builtin_amdgcn_readfirstlane(lo);
@@ -948,9 +961,10 @@ struct EpiPartial {
 };
 
 // C = bf16(sum over s < S of the parts of each tail tile), for tile ids
-// [tile_base, tile_base + tiles) of the tiles_m x tiles_n order; one thread
-// per 8 columns of a tile row, BM * BN / 8 / 256 workgroups per tile.
-template <class T>
+// [tile_base, tile_base + tiles) of the tiles_m x tiles_n order (GM: the
+// group rows of the GEMM that wrote the parts); one thread per 8 columns of a
+// tile row, BM * BN / 8 / 256 workgroups per tile.
+template <class T, int GM>
 __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restrict__ P, int S, int tile_base,
                                                            int tiles_m, int tiles_n, int M, int N,
                                                            uint16_t* __restrict__ C, int64_t ldc) {
@@ -960,7 +974,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
   const int it = (blockIdx.x - t * PER_TILE) * 256 + threadIdx.x;
   const int r = it / (T::BN / 8), c = (it % (T::BN / 8)) * 8;
   int tm, tn;
-  tile_order(tile_base + t, tiles_m, tiles_n, tm, tn);
+  tile_order<GM>(tile_base + t, tiles_m, tiles_n, tm, tn);
   const int row = tm * T::BM + r, col = tn * T::BN + c;
   if (row >= M || col >= N) return;
   f32x8 v = {};

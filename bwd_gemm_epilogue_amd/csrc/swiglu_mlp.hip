@@ -534,7 +534,7 @@ int run_store_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
                      dim3(T::THREADS), 0, st, g, pp);
   SW_TRY(launch_status());
   constexpr int PER_TILE = T::BM * T::BN / 8 / 256;
-  hipLaunchKernelGGL(split_reduce_kernel<T>, dim3((unsigned)(pl.rem * PER_TILE)), dim3(256), 0, st, (const float*)sc.p,
+  hipLaunchKernelGGL((split_reduce_kernel<T, group_rows<A_K>()>), dim3((unsigned)(pl.rem * PER_TILE)), dim3(256), 0, st, (const float*)sc.p,
                      pl.S, pl.full, g.tiles_m, g.tiles_n, (int)M, (int)N, ep.C, ep.ldc);
   return launch_status();
 }
